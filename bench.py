@@ -1,0 +1,387 @@
+"""Benchmark of split-KV grouped-query decode attention on one MI355X.
+
+One step = one hipGraph replay of L layers x (partial kernel + combine kernel)
+of the 28 query / 4 KV head, head_dim 128 decode shape (the 7B shape of
+"10 · R4 — decode split-attention dim-parallel rewrite"), with every layer's
+fp16 KV cache in its own buffer so that the 28 layers (1.9 GB at 32K context)
+stream from HBM rather than from the 256 MB Infinity Cache. The live length is
+set through positions[] on the device; the captured graph is the same for
+every length.
+
+Reported (one JSON line on stdout):
+  value       KV-stream GB/s = algorithmic K+V bytes of the L layers / step time
+              (the effective stream rate of "10 · R4", section 1)
+  us/layer    step time / L (partial + combine + the gap between them)
+  roofline    the partial kernel alone: K+V bytes per launch / its average
+              duration, timed with HIP events on its own stream, against the
+              8 TB/s HBM peak; `traffic` is the HBM bytes per launch measured by
+              rocprofv3 counters (profiles/), or null when the counters were
+              taken on another version of the kernel source
+  cpu_baseline  the fp64 oracle on the host, one core, on one layer
+
+Usage: python bench.py [--steps K] [--warmup W] [--nkv N] [--layers L]
+       python bench.py --sweep          # split-count sweep, one line per point
+       python bench.py --summarize-pmc DIR  # fold rocprofv3 --pmc output
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "KV-stream GB/s (% of HBM peak) + µs/layer, 28q/4kv hd128 decode @2K–32K"
+HBM_PEAK_GBPS = 8000.0
+PARTIAL_SRC = os.path.join(ROOT, "decode_attention_gqa_amd", "csrc",
+                           "splitkv_partial.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partial_hd128_g7_traffic.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(path=PARTIAL_SRC) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+# --------------------------------------------------------------------------
+class Layers:
+    """L layers of the 28q/4kv hd128 cache, each in its own device buffers."""
+
+    def __init__(self, layers: int, max_ctx: int, n_splits: int, block_len: int):
+        import torch
+
+        import decode_attention_gqa_amd as skv
+        import synth
+        self.torch, self.skv = torch, skv
+        sh = synth.Shape(1, 28, 4, 128, max_ctx)
+        self.shape = sh
+        self.L = layers
+        self.S, self.blk = n_splits, block_len
+        log(f"[bench] generating layer data: max_ctx={max_ctx}")
+        case = synth.make_offset_case(3, sh, max_ctx)
+        self.case = case
+        dev = torch.device("cuda", 0)
+        k0 = torch.from_numpy(case.k).to(dev)
+        v0 = torch.from_numpy(case.v).to(dev)
+        q0 = torch.from_numpy(case.q).to(dev)
+        # distinct allocations per layer: same values, different addresses
+        self.k = [k0] + [k0.clone() for _ in range(layers - 1)]
+        self.v = [v0] + [v0.clone() for _ in range(layers - 1)]
+        self.q = [q0.clone() for _ in range(layers)]
+        self.pos = torch.zeros(1, dtype=torch.int32, device=dev)
+        nb = skv.partials_bytes(1, sh.n_head, sh.head_dim, n_splits)
+        self.part = [torch.empty(nb // 4, dtype=torch.float32, device=dev)
+                     for _ in range(layers)]
+        self.out = [torch.empty((1, sh.n_head, sh.head_dim), dtype=torch.float32,
+                                device=dev) for _ in range(layers)]
+        self.scale = case.scale
+        torch.cuda.synchronize()
+
+    def step(self):
+        for l in range(self.L):
+            self.skv.decode_attn(self.q[l], self.k[l], self.v[l], self.pos,
+                                 self.part[l], self.out[l], self.S, self.blk,
+                                 self.scale)
+
+    def partial(self, l):
+        self.skv.partial(self.q[l], self.k[l], self.v[l], self.pos, self.part[l],
+                         self.S, self.blk, self.scale)
+
+    def combine(self, l):
+        self.skv.combine(self.part[l], self.out[l], self.S)
+
+    def capture(self):
+        torch = self.torch
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.step()
+        torch.cuda.synchronize()
+        return g
+
+    def set_nkv(self, nkv: int):
+        self.pos.fill_(nkv - 1)
+        self.torch.cuda.synchronize()
+
+
+def time_replays(torch, graph, warmup: int, steps: int):
+    """Per-replay milliseconds (events on the replay stream) and the total."""
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    stream = torch.cuda.current_stream()
+    t0 = time.perf_counter()
+    evs[0].record(stream)
+    for i in range(steps):
+        graph.replay()
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    total = evs[0].elapsed_time(evs[-1])
+    return per, total, wall
+
+
+def time_kernel(torch, launch, layers: int, reps: int):
+    """Average duration of one launch: events bracket each launch on the
+    stream it runs on, rotating over the layers' buffers."""
+    stream = torch.cuda.current_stream()
+    for l in range(layers):
+        launch(l)
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
+    for i in range(reps):
+        starts[i].record(stream)
+        launch(i % layers)
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    return statistics.mean(ms), statistics.median(ms)
+
+
+def hbm_read_probe(torch, skv, gib: float = 4.0, reps: int = 5) -> float:
+    """Measured HBM read stream rate (GB/s) of a plain 16-byte load kernel."""
+    n = int(gib * (1 << 30))
+    buf = torch.zeros(n // 4, dtype=torch.int32, device="cuda")
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    grid = cu * 16
+    sink = torch.zeros(grid, dtype=torch.int32, device="cuda")
+    skv.probe_read(buf, sink, grid)
+    torch.cuda.synchronize()
+    best = 0.0
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        skv.probe_read(buf, sink, grid)
+        b.record()
+        torch.cuda.synchronize()
+        best = max(best, n / (a.elapsed_time(b) * 1e-3) / 1e9)
+    del buf
+    return best
+
+
+def cpu_baseline(lay: Layers, nkv: int, budget_s: float = 12.0) -> dict:
+    """The fp64 oracle (one thread) on one layer at the same live length."""
+    import numpy as np
+
+    import oracle
+    import synth
+    c = lay.case
+    pos = np.array([nkv - 1], np.int32)
+    kv = synth.kv_bytes(lay.shape.n_kv_head, lay.shape.head_dim, nkv)
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        oracle.decode_attn(c.q, c.k, c.v, pos, lay.shape.n_kv_head, c.scale)
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or runs >= 50:
+            break
+    return {"value": round(kv * runs / el / 1e9, 4), "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{runs} x one layer (28q/4kv hd128, nkv {nkv}) in "
+                      f"{el:.1f} s, single-threaded fp64 C, host "
+                      f"{os.cpu_count()} cpus visible"}
+
+
+def load_traffic(nkv: int, n_splits: int, block_len: int):
+    """HBM bytes per partial launch from the committed counter summary, if it
+    was taken on the current kernel source and the same workload."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None, "no counter summary"
+    with open(TRAFFIC_FILE) as f:
+        t = json.load(f)
+    if t.get("partial_src_sha256_16") != source_hash():
+        return None, "kernel changed since the counters were taken"
+    if (t.get("nkv"), t.get("n_splits"), t.get("block_len")) != (nkv, n_splits,
+                                                                 block_len):
+        return None, "counters taken on another workload"
+    return t.get("hbm_bytes_per_launch"), "rocprofv3 FETCH_SIZE+WRITE_SIZE"
+
+
+# --------------------------------------------------------------------------
+def run_main(args):
+    import torch
+
+    import decode_attention_gqa_amd as skv
+    import synth
+    if not os.path.exists(skv.LIB_PATH):
+        from decode_attention_gqa_amd import build as hip_build
+        hip_build.build()
+    props = torch.cuda.get_device_properties(0)
+    cu = props.multi_processor_count
+    max_ctx = synth.CFG3.max_ctx
+    if args.n_splits:
+        S, blk = args.n_splits, args.block_len
+    else:
+        S, blk = skv.pick_splits(1, 28, 4, 128, max_ctx, cu)
+    lay = Layers(args.layers, max_ctx, S, blk)
+    graph = lay.capture()
+
+    points = []
+    for nkv in sorted(set(args.points + [args.nkv])):
+        lay.set_nkv(nkv)
+        per, total, _ = time_replays(torch, graph, args.warmup, args.steps)
+        med = statistics.median(per)
+        kv = synth.kv_bytes(4, 128, nkv) * args.layers
+        points.append({"nkv": nkv, "ms_per_step_median": round(med, 5),
+                       "us_per_layer": round(med * 1e3 / args.layers, 3),
+                       "kv_gbps": round(kv / (med * 1e-3) / 1e9, 1),
+                       "pct_hbm_peak": round(100 * kv / (med * 1e-3) / 1e9 /
+                                             HBM_PEAK_GBPS, 2)})
+        log(f"[bench] nkv={nkv}: {points[-1]}")
+
+    # headline: the timed K steps at --nkv
+    lay.set_nkv(args.nkv)
+    per, total, wall = time_replays(torch, graph, args.warmup, args.steps)
+    ms_step = total / args.steps
+    kv_layer = synth.kv_bytes(4, 128, args.nkv)
+    value = kv_layer * args.layers / (ms_step * 1e-3) / 1e9
+
+    # dominant kernel alone (partial), and the combine, events on its stream
+    p_mean, p_med = time_kernel(torch, lay.partial, args.layers, args.kernel_reps)
+    c_mean, c_med = time_kernel(torch, lay.combine, args.layers, args.kernel_reps)
+    achieved = kv_layer / (p_mean * 1e-3) / 1e9
+    traffic, traffic_src = load_traffic(args.nkv, S, blk)
+    probe = hbm_read_probe(torch, skv) if not args.no_probe else None
+
+    cpu = cpu_baseline(lay, args.nkv, args.cpu_budget) if not args.no_cpu else None
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"decode attention 28q/4kv hd128, nkv {args.nkv}, "
+                               f"{args.layers} layers with separate KV buffers, "
+                               f"hipGraph of partial+combine",
+                   "nkv": args.nkv, "layers": args.layers, "max_ctx": max_ctx,
+                   "n_splits": S, "block_len": blk, "kv_dtype": "fp16",
+                   "q_acc_dtype": "fp32", "global_batch": 1},
+        "us_per_layer": round(ms_step * 1e3 / args.layers, 3),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic,
+                     "kernel": "partial_kernel<128,7>",
+                     "bytes_per_launch": kv_layer,
+                     "avg_launch_us": round(p_mean * 1e3, 3),
+                     "median_launch_us": round(p_med * 1e3, 3),
+                     "traffic_source": traffic_src},
+        "combine_avg_launch_us": round(c_mean * 1e3, 3),
+        "hbm_read_probe_gbps": round(probe, 1) if probe else None,
+        "points": points,
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 4),
+        "device": props.name,
+        "cu_count": cu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_sweep(args):
+    import torch
+
+    import decode_attention_gqa_amd as skv
+    import synth
+    max_ctx = synth.CFG3.max_ctx
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    for S, blk in [(s, 0) for s in args.sweep_splits] + \
+                  [(-(-max_ctx // b), b) for b in args.sweep_blocks]:
+        lay = Layers(args.layers, max_ctx, S, blk)
+        graph = lay.capture()
+        for nkv in args.points:
+            lay.set_nkv(nkv)
+            per, total, _ = time_replays(torch, graph, args.warmup, args.steps)
+            med = statistics.median(per)
+            kv = synth.kv_bytes(4, 128, nkv) * args.layers
+            print(json.dumps({"sweep": True, "n_splits": S, "block_len": blk,
+                              "nkv": nkv, "cu": cu,
+                              "us_per_layer": round(med * 1e3 / args.layers, 3),
+                              "kv_gbps": round(kv / (med * 1e-3) / 1e9, 1)}),
+                  flush=True)
+        del lay, graph
+        torch.cuda.empty_cache()
+
+
+def summarize_pmc(directory: str, copy_bytes: int | None = None):
+    """Fold rocprofv3 --pmc counter CSVs into per-kernel means (KiB/dispatch)."""
+    rows = {}
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"),
+                          recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                key = (r.get("Kernel_Name", "?"), r.get("Counter_Name", "?"))
+                rows.setdefault(key, []).append(float(r.get("Counter_Value", 0)))
+    out = {}
+    for (k, c), vals in sorted(rows.items()):
+        out.setdefault(k, {})[c] = {"mean": statistics.mean(vals), "n": len(vals)}
+    print(json.dumps(out, indent=1))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--nkv", type=int, default=32768)
+    ap.add_argument("--layers", type=int, default=28)
+    ap.add_argument("--points", type=int, nargs="*",
+                    default=[2048, 4096, 8192, 16384, 32768])
+    ap.add_argument("--n-splits", type=int, default=0)
+    ap.add_argument("--block-len", type=int, default=0)
+    ap.add_argument("--kernel-reps", type=int, default=112)
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--sweep-splits", type=int, nargs="*",
+                    default=[16, 32, 64, 128, 256, 512])
+    ap.add_argument("--sweep-blocks", type=int, nargs="*", default=[128, 256, 512])
+    ap.add_argument("--summarize-pmc", default=None)
+    args = ap.parse_args()
+    if args.summarize_pmc:
+        summarize_pmc(args.summarize_pmc)
+        return 0
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this path has no multi-GPU "
+              "component (sharding by KV head or batch needs no exchange; see "
+              "the design notes)", file=sys.stderr)
+        return 2
+    if args.sweep:
+        run_sweep(args)
+    else:
+        run_main(args)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

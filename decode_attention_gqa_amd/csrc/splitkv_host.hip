@@ -1,0 +1,232 @@
+// splitkv_host.hip -- the C ABI of libsplitkv.so (declared in
+// include/splitkv.h and include/splitkv_probe.h): argument validation, shape
+// dispatch, the split heuristic and the launches. Validation is pure host code
+// and runs before any HIP call, so every error path can be exercised on a
+// machine without a GPU.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <climits>
+#include <cmath>
+
+#include "splitkv.h"
+#include "splitkv_internal.h"
+#include "splitkv_probe.h"
+
+namespace {
+
+constexpr double kLog2e = 1.44269504088896340736;
+constexpr int kMaxSplits = 65535;
+constexpr int kMaxGridYZ = 65535;
+
+bool aligned(const void *p, uintptr_t n) {
+  return (reinterpret_cast<uintptr_t>(p) % n) == 0;
+}
+
+int check_shape(int batch, int n_head, int n_kv_head, int head_dim,
+                int max_ctx, int n_splits, int block_len) {
+  if (batch < 1 || n_head < 1 || n_kv_head < 1 || max_ctx < 1 ||
+      n_splits < 1 || block_len < 0)
+    return SPLITKV_EINVAL;
+  if (n_head % n_kv_head != 0) return SPLITKV_EINVAL;
+  if (!splitkv::head_dim_supported(head_dim)) return SPLITKV_EUNSUPPORTED;
+  if (n_head / n_kv_head > splitkv::kMaxGroup) return SPLITKV_EUNSUPPORTED;
+  if (n_splits > kMaxSplits || n_kv_head > kMaxGridYZ || batch > kMaxGridYZ)
+    return SPLITKV_EINVAL;
+  if ((long long)max_ctx + n_splits >= (long long)INT_MAX) return SPLITKV_EINVAL;
+  // A sequence's K (or V) cache must stay below 4 GiB.
+  if ((long long)max_ctx * n_kv_head * head_dim * 2 >= (1LL << 32))
+    return SPLITKV_EINVAL;
+  if (block_len > 0) {
+    // The fixed-length rule must reach every position the cache can hold.
+    if ((long long)block_len * n_splits < max_ctx) return SPLITKV_EINVAL;
+    if ((long long)block_len * n_splits > (long long)INT_MAX)
+      return SPLITKV_EINVAL;
+  }
+  return SPLITKV_OK;
+}
+
+int check_combine_shape(int batch, int n_head, int head_dim, int n_splits) {
+  if (batch < 1 || n_head < 1 || n_splits < 1) return SPLITKV_EINVAL;
+  if (!splitkv::head_dim_supported(head_dim)) return SPLITKV_EUNSUPPORTED;
+  if (n_splits > kMaxSplits || n_head > kMaxGridYZ || batch > kMaxGridYZ)
+    return SPLITKV_EINVAL;
+  return SPLITKV_OK;
+}
+
+int check_partial(const float *q, const uint16_t *k, const uint16_t *v,
+                  const int32_t *positions, const float *partials, int batch,
+                  int n_head, int n_kv_head, int head_dim, int max_ctx,
+                  int n_splits, int block_len, float scale) {
+  if (!q || !k || !v || !positions || !partials) return SPLITKV_EINVAL;
+  const int st = check_shape(batch, n_head, n_kv_head, head_dim, max_ctx,
+                             n_splits, block_len);
+  if (st != SPLITKV_OK) return st;
+  if (!std::isfinite(scale)) return SPLITKV_EINVAL;
+  if (!aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) ||
+      !aligned(partials, 16) || !aligned(positions, 4))
+    return SPLITKV_EALIGN;
+  return SPLITKV_OK;
+}
+
+int check_combine(const float *partials, const float *out, int batch,
+                  int n_head, int head_dim, int n_splits) {
+  if (!partials || !out) return SPLITKV_EINVAL;
+  const int st = check_combine_shape(batch, n_head, head_dim, n_splits);
+  if (st != SPLITKV_OK) return st;
+  if (!aligned(partials, 16) || !aligned(out, 16)) return SPLITKV_EALIGN;
+  return SPLITKV_OK;
+}
+
+int do_partial(const float *q, const uint16_t *k, const uint16_t *v,
+               const int32_t *positions, float *partials, int batch,
+               int n_head, int n_kv_head, int head_dim, int max_ctx,
+               int n_splits, int block_len, float scale, void *stream) {
+  splitkv::PartialArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.positions = positions;
+  a.partials = partials;
+  a.n_head = n_head;
+  a.n_kv_head = n_kv_head;
+  a.max_ctx = max_ctx;
+  a.n_splits = n_splits;
+  a.block_len = block_len;
+  a.scale_log2 = (float)((double)scale * kLog2e);
+  const hipError_t e =
+      splitkv::launch_partial(head_dim, n_head / n_kv_head, a, batch,
+                              static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPLITKV_OK : SPLITKV_ELAUNCH;
+}
+
+int do_combine(const float *partials, float *out, int batch, int n_head,
+               int head_dim, int n_splits, void *stream) {
+  splitkv::CombineArgs a;
+  a.partials = partials;
+  a.out = out;
+  a.n_head = n_head;
+  a.n_splits = n_splits;
+  const hipError_t e = splitkv::launch_combine(
+      head_dim, a, batch, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SPLITKV_OK : SPLITKV_ELAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int splitkv_abi_version(void) { return SPLITKV_ABI_VERSION; }
+
+const char *splitkv_strerror(int status) {
+  switch (status) {
+    case SPLITKV_OK: return "ok";
+    case SPLITKV_EINVAL: return "invalid argument";
+    case SPLITKV_EUNSUPPORTED: return "unsupported head_dim or group size";
+    case SPLITKV_EALIGN: return "misaligned pointer";
+    case SPLITKV_ELAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+size_t splitkv_partials_bytes(int batch, int n_head, int head_dim,
+                              int n_splits) {
+  if (batch < 1 || n_head < 1 || head_dim < 1 || n_splits < 1) return 0;
+  return (size_t)batch * (size_t)n_splits * (size_t)n_head *
+         (size_t)(4 + head_dim) * sizeof(float);
+}
+
+int splitkv_pick_splits(int batch, int n_head, int n_kv_head, int head_dim,
+                        int max_ctx, int cu_count, int *n_splits,
+                        int *block_len) {
+  if (!n_splits || !block_len || cu_count < 1) return SPLITKV_EINVAL;
+  const int st =
+      check_shape(batch, n_head, n_kv_head, head_dim, max_ctx, 1, 0);
+  if (st != SPLITKV_OK) return st;
+  const int group = n_head / n_kv_head;
+  // Enough workgroups for two per compute unit over the whole grid ...
+  const long long units = (long long)batch * n_kv_head;
+  const long long target = 2LL * cu_count;
+  long long s = (target + units - 1) / units;
+  // ... while a full-length split keeps at least 16 rows per query head of
+  // the group, so the per-split fixed costs stay amortised.
+  const long long min_rows = 16LL * group > 64 ? 16LL * group : 64;
+  const long long cap = max_ctx / min_rows > 1 ? max_ctx / min_rows : 1;
+  if (s > cap) s = cap;
+  if (s < 1) s = 1;
+  if (s > kMaxSplits) s = kMaxSplits;
+  *n_splits = (int)s;
+  *block_len = 0;
+  return SPLITKV_OK;
+}
+
+int splitkv_partial(const float *q, const uint16_t *k_cache,
+                    const uint16_t *v_cache, const int32_t *positions,
+                    float *partials, int batch, int n_head, int n_kv_head,
+                    int head_dim, int max_ctx, int n_splits, int block_len,
+                    float scale, void *stream) {
+  const int st = check_partial(q, k_cache, v_cache, positions, partials, batch,
+                               n_head, n_kv_head, head_dim, max_ctx, n_splits,
+                               block_len, scale);
+  if (st != SPLITKV_OK) return st;
+  return do_partial(q, k_cache, v_cache, positions, partials, batch, n_head,
+                    n_kv_head, head_dim, max_ctx, n_splits, block_len, scale,
+                    stream);
+}
+
+int splitkv_combine(const float *partials, float *out, int batch, int n_head,
+                    int head_dim, int n_splits, void *stream) {
+  const int st =
+      check_combine(partials, out, batch, n_head, head_dim, n_splits);
+  if (st != SPLITKV_OK) return st;
+  return do_combine(partials, out, batch, n_head, head_dim, n_splits, stream);
+}
+
+int splitkv_decode_attn(const float *q, const uint16_t *k_cache,
+                        const uint16_t *v_cache, const int32_t *positions,
+                        float *partials, float *out, int batch, int n_head,
+                        int n_kv_head, int head_dim, int max_ctx, int n_splits,
+                        int block_len, float scale, void *stream) {
+  int st = check_partial(q, k_cache, v_cache, positions, partials, batch,
+                         n_head, n_kv_head, head_dim, max_ctx, n_splits,
+                         block_len, scale);
+  if (st != SPLITKV_OK) return st;
+  st = check_combine(partials, out, batch, n_head, head_dim, n_splits);
+  if (st != SPLITKV_OK) return st;
+  st = do_partial(q, k_cache, v_cache, positions, partials, batch, n_head,
+                  n_kv_head, head_dim, max_ctx, n_splits, block_len, scale,
+                  stream);
+  if (st != SPLITKV_OK) return st;
+  return do_combine(partials, out, batch, n_head, head_dim, n_splits, stream);
+}
+
+int splitkv_probe_read(const void *buf, size_t bytes, uint32_t *sink,
+                       int grid, void *stream) {
+  if (!buf || !sink || bytes == 0 || bytes % 16 != 0 || grid < 1 ||
+      grid > (1 << 20))
+    return SPLITKV_EINVAL;
+  if (!aligned(buf, 16) || !aligned(sink, 4)) return SPLITKV_EALIGN;
+  return splitkv::launch_probe_read(buf, bytes, sink, grid,
+                                    static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? SPLITKV_OK
+             : SPLITKV_ELAUNCH;
+}
+
+int splitkv_probe_copy(const void *src, void *dst, size_t bytes, int grid,
+                       void *stream) {
+  if (!src || !dst || bytes == 0 || bytes % 16 != 0 || grid < 1 ||
+      grid > (1 << 20))
+    return SPLITKV_EINVAL;
+  if (!aligned(src, 16) || !aligned(dst, 16)) return SPLITKV_EALIGN;
+  const uintptr_t s = reinterpret_cast<uintptr_t>(src);
+  const uintptr_t d = reinterpret_cast<uintptr_t>(dst);
+  if (s < d + bytes && d < s + bytes) return SPLITKV_EINVAL;  // overlap
+  return splitkv::launch_probe_copy(src, dst, bytes, grid,
+                                    static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? SPLITKV_OK
+             : SPLITKV_ELAUNCH;
+}
+
+}  // extern "C"

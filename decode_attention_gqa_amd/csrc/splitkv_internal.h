@@ -1,0 +1,50 @@
+// splitkv_internal.h -- declarations shared by the library's own HIP sources
+// (kernel launchers and the C-ABI host code). Not installed, not part of the
+// ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace splitkv {
+
+// Arguments of the partial kernel, passed by value.
+struct PartialArgs {
+  const float *q;            // [B][n_head][HD] fp32
+  const uint16_t *k;         // [B][max_ctx][n_kv_head][HD] fp16 bits
+  const uint16_t *v;         // same layout
+  const int32_t *positions;  // [B]
+  float *partials;           // [B][n_splits][n_head][4 + HD]
+  int n_head;
+  int n_kv_head;
+  int max_ctx;
+  int n_splits;
+  int block_len;             // 0: chunk = ceil(nkv / n_splits)
+  float scale_log2;          // scale * log2(e): scores are kept in base-2 units
+};
+
+struct CombineArgs {
+  const float *partials;
+  float *out;                // [B][n_head][HD]
+  int n_head;
+  int n_splits;
+};
+
+// Launchers: enqueue one kernel on `stream` and return hipGetLastError().
+// The host code validates every argument before calling them.
+hipError_t launch_partial(int head_dim, int group, const PartialArgs &a,
+                          int batch, hipStream_t stream);
+hipError_t launch_combine(int head_dim, const CombineArgs &a, int batch,
+                          hipStream_t stream);
+hipError_t launch_probe_read(const void *buf, size_t bytes, uint32_t *sink,
+                             int grid, hipStream_t stream);
+hipError_t launch_probe_copy(const void *src, void *dst, size_t bytes,
+                             int grid, hipStream_t stream);
+
+// Compiled shapes.
+constexpr bool head_dim_supported(int hd) {
+  return hd == 8 || hd == 16 || hd == 32 || hd == 64 || hd == 128 || hd == 256;
+}
+constexpr int kMaxGroup = 8;
+
+}  // namespace splitkv

@@ -1,0 +1,128 @@
+/*
+ * splitkv.h -- C ABI of the MI355X (gfx950) split-KV grouped-query decode
+ * attention library (libsplitkv.so).
+ *
+ * The operation ("10 · R4 — decode split-attention dim-parallel rewrite",
+ * section 2.1): for every sequence b and query head h, with one query row per
+ * head,
+ *     o[b][h] = softmax(scale * q[b][h] · K[b][0:nkv_b][h/G]ᵀ) · V[b][0:nkv_b][h/G]
+ * over an fp16 KV cache, computed in two stages: a partial kernel runs an
+ * online softmax over each split's row range and writes one (mx, S, oc)
+ * record per (sequence, split, query head); a combine kernel merges the
+ * records ("10 · R4", sections 2.1 and 3.2). One workgroup of the partial
+ * kernel serves one (split, KV head, sequence) and computes all G query heads
+ * of that KV head, so every K/V row is read from HBM once per group ("Red Lite
+ * dev35 — long-context decode: grouped split-K attention", Change).
+ *
+ * Common conventions for every entry point:
+ *  - All array arguments are DEVICE pointers owned by the caller. The library
+ *    allocates nothing, never synchronises, and only enqueues work on
+ *    `stream` (a hipStream_t passed as void*; NULL is the null stream), so the
+ *    calls may be captured into a hipGraph.
+ *  - The live length of sequence b is read on the device at run time:
+ *    nkv_b = clamp(positions[b] + 1, 0, max_ctx) ("10 · R4", section 2.2).
+ *    Launch geometry never depends on it, so one captured graph stays valid as
+ *    positions[] advances. positions[] is only read.
+ *  - Query head h reads KV head h / G, G = n_head / n_kv_head (contiguous
+ *    groups).
+ *  - Every argument is validated on the host before any HIP call; on error
+ *    nothing is enqueued and a negative status is returned. Nothing throws.
+ *  - The functions are reentrant and keep no state. Calls that share a
+ *    `partials` buffer must be ordered on one stream.
+ *
+ * Layouts (row-major, innermost last):
+ *   q         float32  [batch][n_head][head_dim]            16-byte aligned
+ *   k_cache   fp16     [batch][max_ctx][n_kv_head][head_dim] 16-byte aligned
+ *   v_cache   fp16     same as k_cache                       16-byte aligned
+ *             (row of position p, KV head g starts at element
+ *              ((b*max_ctx + p)*n_kv_head + g)*head_dim; "10 · R4", section 3.2
+ *              addresses it as pos*stride_kv + hk*hd, read here as
+ *              stride_kv = n_kv_head*head_dim); fp16 values are passed as their
+ *              IEEE binary16 bit patterns (uint16_t).
+ *   positions int32    [batch]                               4-byte aligned
+ *   partials  float32  [batch][n_splits][n_head][4 + head_dim] 16-byte aligned
+ *             record = { mx, S, lo, hi, oc[0..head_dim) }: mx is the largest
+ *             score of the split (natural-log units, -inf when the split is
+ *             idle), S the sum of exp(score - mx), oc the exp-weighted V sum
+ *             (not normalised), lo/hi the split's row range as int32 bit
+ *             patterns ("10 · R4", sections 2.1 and 3.2; slots 2 and 3 are
+ *             unused padding on the page).
+ *   out       float32  [batch][n_head][head_dim]             16-byte aligned
+ *
+ * Split rule ("10 · R4", section 2.2; "Red Lite dev35", Change): with
+ * block_len == 0, chunk = ceil(nkv_b / n_splits); with block_len > 0, chunk =
+ * block_len (requires block_len * n_splits >= max_ctx). Split sp covers rows
+ * [sp*chunk, min(nkv_b, sp*chunk + chunk)); a split with no rows writes
+ * (-inf, 0, lo, hi, 0...) and contributes exactly zero to the merge.
+ *
+ * Supported shapes: head_dim in {8, 16, 32, 64, 128, 256}; G = n_head /
+ * n_kv_head in 1..8; n_splits in 1..65535; n_kv_head and batch <= 65535;
+ * max_ctx + n_splits < 2^31; a sequence's K (or V) cache below 4 GiB.
+ */
+#ifndef SPLITKV_H
+#define SPLITKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define SPLITKV_OK 0
+#define SPLITKV_EINVAL (-1)       /* null pointer, bad size, bad split rule   */
+#define SPLITKV_EUNSUPPORTED (-2) /* head_dim or group size not compiled      */
+#define SPLITKV_EALIGN (-3)       /* a pointer breaks its alignment rule      */
+#define SPLITKV_ELAUNCH (-4)      /* the HIP runtime refused a launch         */
+
+#define SPLITKV_ABI_VERSION 1
+
+/* ABI version of the loaded library (SPLITKV_ABI_VERSION at build time). */
+int splitkv_abi_version(void);
+
+/* Human-readable text for a status code; never NULL, static storage. */
+const char *splitkv_strerror(int status);
+
+/* Bytes the caller must provide for `partials`:
+ * batch * n_splits * n_head * (4 + head_dim) * 4. Returns 0 for any
+ * non-positive argument. */
+size_t splitkv_partials_bytes(int batch, int n_head, int head_dim,
+                              int n_splits);
+
+/* Split heuristic: chooses n_splits (and block_len, 0 = ceil rule) for a
+ * shape, from the sequence capacity max_ctx and the GPU's compute-unit count.
+ * The aim, from the pages: enough workgroups to fill the GPU ("10 · R4",
+ * sections 1 and 3.1; dotLLM issue #199, comment 2, recommendation 1) while
+ * each split keeps enough rows that its fixed costs (query load, record
+ * write, merge) stay small ("10 · R4", section 3.3; "Red Lite dev35", the
+ * block-length table). Host only; returns SPLITKV_OK or a negative status. */
+int splitkv_pick_splits(int batch, int n_head, int n_kv_head, int head_dim,
+                        int max_ctx, int cu_count, int *n_splits,
+                        int *block_len);
+
+/* Partial kernel only: writes every record of `partials`. */
+int splitkv_partial(const float *q, const uint16_t *k_cache,
+                    const uint16_t *v_cache, const int32_t *positions,
+                    float *partials, int batch, int n_head, int n_kv_head,
+                    int head_dim, int max_ctx, int n_splits, int block_len,
+                    float scale, void *stream);
+
+/* Combine kernel only: merges the records into `out` ("10 · R4", section 2.1:
+ * gmx = max mx, w = exp(mx - gmx), o = sum w*oc / sum w*S, 0 when the weight
+ * sum is not positive; a record with mx = -inf has weight 0). */
+int splitkv_combine(const float *partials, float *out, int batch, int n_head,
+                    int head_dim, int n_splits, void *stream);
+
+/* The whole operation: splitkv_partial then splitkv_combine on `stream`. */
+int splitkv_decode_attn(const float *q, const uint16_t *k_cache,
+                        const uint16_t *v_cache, const int32_t *positions,
+                        float *partials, float *out, int batch, int n_head,
+                        int n_kv_head, int head_dim, int max_ctx, int n_splits,
+                        int block_len, float scale, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPLITKV_H */

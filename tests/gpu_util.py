@@ -1,0 +1,101 @@
+"""Helpers for the GPU parity tests: move a synthetic case to the device, run
+the HIP path through the C ABI, and compare with the oracle element by element.
+
+Parity bar (per element): |gpu - oracle| <= 5e-5, or <= 1e-3 * |oracle|. Integer
+outputs (split bounds) must be bit-exact.
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+ABS_TOL = 5e-5
+REL_TOL = 1e-3
+
+
+def say(*parts):
+    """Name the case about to run on the GPU, flushed, so a crash log shows it."""
+    print("[gpu-case]", *parts, flush=True)
+    sys.stdout.flush()
+
+
+def torch_mod():
+    import torch
+    if not torch.cuda.is_available():
+        raise RuntimeError("GPU tests need a GPU")
+    return torch
+
+
+def to_device(case):
+    torch = torch_mod()
+    dev = torch.device("cuda", 0)
+    q = torch.from_numpy(np.ascontiguousarray(case.q)).to(dev)
+    k = torch.from_numpy(np.ascontiguousarray(case.k)).to(dev)
+    v = torch.from_numpy(np.ascontiguousarray(case.v)).to(dev)
+    pos = torch.from_numpy(np.ascontiguousarray(case.positions, np.int32)).to(dev)
+    return q, k, v, pos
+
+
+def alloc_outputs(shape, n_splits):
+    import decode_attention_gqa_amd as skv
+    torch = torch_mod()
+    nbytes = skv.partials_bytes(shape.batch, shape.n_head, shape.head_dim,
+                                n_splits)
+    part = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda")
+    part.fill_(float("nan"))   # every record must be written by the kernel
+    out = torch.empty((shape.batch, shape.n_head, shape.head_dim),
+                      dtype=torch.float32, device="cuda")
+    out.fill_(float("nan"))
+    return part, out
+
+
+def run_gpu(case, n_splits, block_len=0, dev=None):
+    """decode_attn through the C ABI; returns (out, records) as numpy."""
+    import decode_attention_gqa_amd as skv
+    torch = torch_mod()
+    sh = case.shape
+    q, k, v, pos = dev if dev is not None else to_device(case)
+    part, out = alloc_outputs(sh, n_splits)
+    skv.decode_attn(q, k, v, pos, part, out, n_splits, block_len, case.scale)
+    torch.cuda.synchronize()
+    rec = part.cpu().numpy().reshape(sh.batch, n_splits, sh.n_head,
+                                     4 + sh.head_dim)
+    return out.cpu().numpy(), rec
+
+
+def parity(got, ref, what=""):
+    """Assert the parity bar; returns (max abs err, max rel err)."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert not np.isnan(got).any(), f"{what}: NaN in GPU output"
+    err = np.abs(got - ref)
+    rel = err / np.maximum(np.abs(ref), 1e-30)
+    ok = (err <= ABS_TOL) | (err <= REL_TOL * np.abs(ref))
+    if not ok.all():
+        idx = np.unravel_index(np.argmax(np.where(ok, 0, err)), err.shape)
+        raise AssertionError(
+            f"{what}: {int((~ok).sum())} of {ok.size} outside the bar; worst at "
+            f"{idx}: gpu {got[idx]!r} oracle {ref[idx]!r} abs {err[idx]:.3e}")
+    return float(err.max()) if err.size else 0.0, \
+        float(np.where(np.abs(ref) > 1e-6, rel, 0).max()) if rel.size else 0.0
+
+
+def check_records(rec_gpu, rec_ref, what=""):
+    """Records: lo/hi bit-exact, idle slots exact, mx / S / oc/S within the bar."""
+    lohi = rec_gpu[..., 2:4].copy().view(np.int32)
+    assert np.array_equal(lohi, rec_ref[..., 2:4].astype(np.int32)), \
+        f"{what}: split bounds differ"
+    idle = rec_ref[..., 0] == -np.inf
+    assert np.array_equal(rec_gpu[..., 0] == -np.inf, idle), \
+        f"{what}: idle pattern differs"
+    assert np.all(rec_gpu[..., 1][idle] == 0.0)
+    assert np.all(rec_gpu[..., 4:][idle] == 0.0)
+    live = ~idle
+    if live.any():
+        parity(rec_gpu[..., 0][live], rec_ref[..., 0][live], what + " mx")
+        parity(rec_gpu[..., 1][live], rec_ref[..., 1][live], what + " S")
+        parity(rec_gpu[..., 4:][live] / rec_gpu[..., 1][live][:, None],
+               rec_ref[..., 4:][live] / rec_ref[..., 1][live][:, None],
+               what + " oc/S")

@@ -1,0 +1,192 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+headers declare, reports sizes, runs the split heuristic, and rejects every
+bad argument with its status code before any HIP call.
+"""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+import decode_attention_gqa_amd as skv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+OK, EINVAL, EUNSUP, EALIGN, ELAUNCH = 0, -1, -2, -3, -4
+
+
+def _declared_symbols():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"\b(splitkv_\w+)\s*\(", text))
+    return sorted(names)
+
+
+@pytest.fixture(scope="module")
+def lib(splitkv_lib_path):
+    return skv.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = _declared_symbols()
+    assert "splitkv_decode_attn" in declared and len(declared) >= 9
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(skv.SIGNATURES)
+
+
+def test_version_and_strerror(lib):
+    assert lib.splitkv_abi_version() == 1
+    texts = {c: skv.strerror(c) for c in (OK, EINVAL, EUNSUP, EALIGN, ELAUNCH)}
+    assert len(set(texts.values())) == 5
+    assert skv.strerror(-99) == "unknown status"
+
+
+def test_partials_bytes(lib):
+    # batch * n_splits * n_head * (4 + hd) * 4
+    assert skv.partials_bytes(1, 28, 128, 32) == 32 * 28 * 132 * 4
+    assert skv.partials_bytes(32, 32, 128, 7) == 32 * 7 * 32 * 132 * 4
+    assert skv.partials_bytes(0, 28, 128, 32) == 0
+    assert skv.partials_bytes(1, 28, 128, -1) == 0
+
+
+def test_pick_splits_properties(lib):
+    for shape in [(1, 28, 4, 128, 2048), (1, 28, 4, 128, 33024),
+                  (1, 16, 2, 256, 8400), (32, 32, 8, 128, 32768),
+                  (1, 4, 2, 64, 256), (1, 4, 2, 8, 1024)]:
+        B, nh, nkvh, hd, T = shape
+        S, blk = skv.pick_splits(*shape, cu_count=256)
+        assert 1 <= S <= 65535 and blk >= 0
+        if blk:
+            assert blk * S >= T
+        # never so many splits that a full-length split is tiny
+        assert S == 1 or T // S >= 16
+    with pytest.raises(skv.SplitKVError):
+        skv.pick_splits(1, 28, 5, 128, 2048, 256)      # 28 % 5 != 0
+    with pytest.raises(skv.SplitKVError):
+        skv.pick_splits(1, 28, 4, 96, 2048, 256)       # head_dim not compiled
+    with pytest.raises(skv.SplitKVError):
+        skv.pick_splits(1, 28, 4, 128, 2048, 0)        # no compute units
+
+
+# Fake, aligned addresses: every case below must fail validation, so nothing
+# is ever dereferenced or launched. As a second guard these cases only run on
+# hosts without a GPU, where a launch could not reach a device anyway.
+A = 0x10000
+
+
+def _has_gpu():
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+cpu_only = pytest.mark.skipif(_has_gpu(), reason="raw-pointer validation "
+                              "cases run on GPU-less hosts only")
+
+
+def _partial_args(**over):
+    args = dict(q=A, k=A + 0x1000, v=A + 0x2000, pos=A + 0x3000,
+                part=A + 0x4000, B=1, nh=28, nkvh=4, hd=128, T=2048, S=32,
+                blk=0, scale=0.088)
+    args.update(over)
+    return args
+
+
+def _call_partial(lib, a):
+    return lib.splitkv_partial(a["q"], a["k"], a["v"], a["pos"], a["part"],
+                               a["B"], a["nh"], a["nkvh"], a["hd"], a["T"],
+                               a["S"], a["blk"], a["scale"], None)
+
+
+def _call_decode(lib, a, out=A + 0x5000):
+    return lib.splitkv_decode_attn(a["q"], a["k"], a["v"], a["pos"], a["part"],
+                                   out, a["B"], a["nh"], a["nkvh"], a["hd"],
+                                   a["T"], a["S"], a["blk"], a["scale"], None)
+
+
+BAD_PARTIAL = [
+    ("null q", dict(q=0), EINVAL),
+    ("null k", dict(k=0), EINVAL),
+    ("null v", dict(v=0), EINVAL),
+    ("null positions", dict(pos=0), EINVAL),
+    ("null partials", dict(part=0), EINVAL),
+    ("batch 0", dict(B=0), EINVAL),
+    ("n_head 0", dict(nh=0), EINVAL),
+    ("n_kv_head 0", dict(nkvh=0), EINVAL),
+    ("max_ctx 0", dict(T=0), EINVAL),
+    ("n_splits 0", dict(S=0), EINVAL),
+    ("n_splits too big", dict(S=65536), EINVAL),
+    ("negative block_len", dict(blk=-1), EINVAL),
+    ("heads not divisible", dict(nkvh=3), EINVAL),
+    ("block rule too short", dict(S=8, blk=128), EINVAL),
+    ("block rule overflow", dict(S=65535, blk=1 << 20), EINVAL),
+    ("max_ctx near int max", dict(T=2**31 - 10, nh=1, nkvh=1, hd=8, S=16),
+     EINVAL),
+    ("sequence cache >= 4 GiB", dict(T=2**24, nh=1, nkvh=1, hd=128), EINVAL),
+    ("non-finite scale", dict(scale=float("inf")), EINVAL),
+    ("nan scale", dict(scale=float("nan")), EINVAL),
+    ("head_dim 96", dict(hd=96), EUNSUP),
+    ("head_dim 512", dict(hd=512), EUNSUP),
+    ("group 9", dict(nh=36, nkvh=4), EUNSUP),
+    ("q misaligned", dict(q=A + 4), EALIGN),
+    ("k misaligned", dict(k=A + 0x1000 + 2), EALIGN),
+    ("v misaligned", dict(v=A + 0x2000 + 8), EALIGN),
+    ("partials misaligned", dict(part=A + 0x4000 + 4), EALIGN),
+    ("positions misaligned", dict(pos=A + 0x3000 + 2), EALIGN),
+]
+
+
+@cpu_only
+@pytest.mark.parametrize("what,over,code", BAD_PARTIAL,
+                         ids=[c[0] for c in BAD_PARTIAL])
+def test_partial_rejects(lib, what, over, code):
+    a = _partial_args(**over)
+    assert _call_partial(lib, a) == code
+    assert _call_decode(lib, a) == code
+
+
+@cpu_only
+def test_decode_rejects_bad_out(lib):
+    a = _partial_args()
+    assert _call_decode(lib, a, out=0) == EINVAL
+    assert _call_decode(lib, a, out=A + 0x5000 + 4) == EALIGN
+
+
+BAD_COMBINE = [
+    ("null partials", (0, A + 0x100, 1, 28, 128, 32), EINVAL),
+    ("null out", (A, 0, 1, 28, 128, 32), EINVAL),
+    ("batch 0", (A, A + 0x100, 0, 28, 128, 32), EINVAL),
+    ("n_head 0", (A, A + 0x100, 1, 0, 128, 32), EINVAL),
+    ("n_splits 0", (A, A + 0x100, 1, 28, 128, 0), EINVAL),
+    ("head_dim 48", (A, A + 0x100, 1, 28, 48, 32), EUNSUP),
+    ("partials misaligned", (A + 4, A + 0x100, 1, 28, 128, 32), EALIGN),
+    ("out misaligned", (A, A + 0x104, 1, 28, 128, 32), EALIGN),
+]
+
+
+@cpu_only
+@pytest.mark.parametrize("what,args,code", BAD_COMBINE,
+                         ids=[c[0] for c in BAD_COMBINE])
+def test_combine_rejects(lib, what, args, code):
+    assert lib.splitkv_combine(*args, None) == code
+
+
+@cpu_only
+def test_probe_rejects(lib):
+    assert lib.splitkv_probe_read(0, 16, A, 1, None) == EINVAL
+    assert lib.splitkv_probe_read(A, 17, A + 0x100, 1, None) == EINVAL
+    assert lib.splitkv_probe_read(A, 16, A + 0x100, 0, None) == EINVAL
+    assert lib.splitkv_probe_read(A + 8, 16, A + 0x100, 1, None) == EALIGN
+    assert lib.splitkv_probe_copy(A, A + 8, 32, 1, None) in (EINVAL, EALIGN)
+    assert lib.splitkv_probe_copy(A, A + 16, 32, 1, None) == EINVAL  # overlap
+    assert lib.splitkv_probe_copy(A, 0, 32, 1, None) == EINVAL
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        skv.load(str(tmp_path / "nope.so"))
