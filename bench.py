@@ -42,8 +42,10 @@ if ROOT not in sys.path:
 
 METRIC = "KV-stream GB/s (% of HBM peak) + µs/layer, 28q/4kv hd128 decode @2K–32K"
 HBM_PEAK_GBPS = 8000.0
-PARTIAL_SRC = os.path.join(ROOT, "decode_attention_gqa_amd", "csrc",
-                           "splitkv_partial.hip")
+CSRC = os.path.join(ROOT, "decode_attention_gqa_amd", "csrc")
+PARTIAL_SRCS = [os.path.join(CSRC, f) for f in (
+    "splitkv_partial.hip", "splitkv_partial_mfma.hip",
+    "splitkv_partial_common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partial_hd128_g7_traffic.json")
 
 
@@ -51,9 +53,12 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def source_hash(path=PARTIAL_SRC) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_hash(paths=PARTIAL_SRCS) -> str:
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 # --------------------------------------------------------------------------
@@ -307,6 +312,37 @@ def run_main(args):
     print(json.dumps(line), flush=True)
 
 
+def run_kernels(args):
+    """Counter-collection workload: each layer's partial and combine launched
+    eagerly, then a plain copy of known size (the counter scale)."""
+    import torch
+
+    import decode_attention_gqa_amd as skv
+    import synth
+    max_ctx = synth.CFG3.max_ctx
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    if args.n_splits:
+        S, blk = args.n_splits, args.block_len
+    else:
+        S, blk = skv.pick_splits(1, 28, 4, 128, max_ctx, cu)
+    lay = Layers(args.layers, max_ctx, S, blk)
+    lay.set_nkv(args.nkv)
+    for _ in range(args.steps):
+        for l in range(args.layers):
+            lay.partial(l)
+            lay.combine(l)
+    nbytes = args.copy_mib << 20
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    skv.probe_copy(src, dst, cu * 16)
+    torch.cuda.synchronize()
+    print(json.dumps({"mode": "kernels", "nkv": args.nkv, "n_splits": S,
+                      "block_len": blk, "layers": args.layers,
+                      "steps": args.steps, "copy_bytes": nbytes,
+                      "kv_bytes_per_partial": synth.kv_bytes(4, 128, args.nkv),
+                      "partial_src_sha256_16": source_hash()}), flush=True)
+
+
 def run_sweep(args):
     import torch
 
@@ -367,6 +403,8 @@ def main():
                     default=[16, 32, 64, 128, 256, 512])
     ap.add_argument("--sweep-blocks", type=int, nargs="*", default=[128, 256, 512])
     ap.add_argument("--summarize-pmc", default=None)
+    ap.add_argument("--mode", choices=["main", "kernels"], default="main")
+    ap.add_argument("--copy-mib", type=int, default=256)
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc)
@@ -378,6 +416,8 @@ def main():
         return 2
     if args.sweep:
         run_sweep(args)
+    elif args.mode == "kernels":
+        run_kernels(args)
     else:
         run_main(args)
     return 0

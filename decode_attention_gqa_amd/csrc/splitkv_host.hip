@@ -34,8 +34,9 @@ int check_shape(int batch, int n_head, int n_kv_head, int head_dim,
   if (n_splits > kMaxSplits || n_kv_head > kMaxGridYZ || batch > kMaxGridYZ)
     return SPLITKV_EINVAL;
   if ((long long)max_ctx + n_splits >= (long long)INT_MAX) return SPLITKV_EINVAL;
-  // A sequence's K (or V) cache must stay below 4 GiB.
-  if ((long long)max_ctx * n_kv_head * head_dim * 2 >= (1LL << 32))
+  // A sequence's K (or V) cache, plus one tile of rows past its end, must
+  // stay below 4 GiB: the kernels address it with 32-bit byte offsets.
+  if (((long long)max_ctx + 64) * n_kv_head * head_dim * 2 >= (1LL << 32))
     return SPLITKV_EINVAL;
   if (block_len > 0) {
     // The fixed-length rule must reach every position the cache can hold.

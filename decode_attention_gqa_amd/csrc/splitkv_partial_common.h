@@ -1,0 +1,120 @@
+// splitkv_partial_common.h -- device helpers shared by the two partial
+// kernels (the VALU kernel for head_dim 8/16/32 and the MFMA kernel for
+// head_dim 64/128/256): live length and split bounds, exp2, DPP moves, the
+// exact merge of online-softmax states, and the workgroup's final merge that
+// writes one record per query head.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "splitkv_internal.h"
+
+namespace splitkv {
+namespace detail {
+
+constexpr float kLn2 = 0.693147180559945309417f;
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+
+__device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
+
+__device__ __forceinline__ float fast_exp2(float x) {
+  return __builtin_amdgcn_exp2f(x);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF,
+                                      0xF, false));
+}
+
+// Rows [lo, hi) of split `sp` of sequence `b` ("10 · R4 — decode
+// split-attention dim-parallel rewrite", section 2.2; "Red Lite dev35",
+// Change, for the fixed block length). The live length is read from device
+// memory; every thread of the workgroup computes the same values.
+struct SplitRange {
+  long long lo;
+  long long hi;
+};
+
+__device__ __forceinline__ SplitRange split_range(const PartialArgs &a,
+                                                  int sp, int b) {
+  long long nkv = (long long)a.positions[b] + 1;
+  nkv = nkv < 0 ? 0 : (nkv > a.max_ctx ? a.max_ctx : nkv);
+  const long long chunk =
+      a.block_len > 0 ? (long long)a.block_len
+                      : (nkv + a.n_splits - 1) / a.n_splits;
+  SplitRange r;
+  r.lo = (long long)sp * chunk;
+  const long long h = r.lo + chunk;
+  r.hi = h < nkv ? h : nkv;
+  return r;
+}
+
+// Merge (m2, s2) into (m, s) and return the weights (c1, c2) applied to the
+// two accumulators; base-2 units; a -inf state has weight exactly 0.
+struct MergeW {
+  float c1;
+  float c2;
+};
+__device__ __forceinline__ MergeW merge_weights(float &m, float &s, float m2,
+                                                float s2) {
+  const float mn = fmaxf(m, m2);
+  MergeW w;
+  w.c1 = (m == neg_inf()) ? 0.0f : fast_exp2(m - mn);
+  w.c2 = (m2 == neg_inf()) ? 0.0f : fast_exp2(m2 - mn);
+  s = s * w.c1 + s2 * w.c2;
+  m = mn;
+  return w;
+}
+
+// Final step of a partial workgroup: the kWaves per-wave states in LDS
+// (max and sum per head in base-2 units, unnormalised output per head and
+// dim) are merged exactly and written as records
+// { mx (natural-log units), S, lo, hi, oc[0..HD) } for the G query heads of
+// KV head hk. Must be called by all threads after a barrier.
+template <int HD, int G>
+__device__ __forceinline__ void write_records(
+    const PartialArgs &a, int sp, int hk, int b, const SplitRange &rg,
+    const float (&sm_m)[kWaves][G], const float (&sm_s)[kWaves][G],
+    const float (&sm_o)[kWaves][G][HD]) {
+  const size_t pstr = 4 + HD;
+  float *rec0 = a.partials +
+                (((size_t)b * a.n_splits + sp) * a.n_head + (size_t)hk * G) *
+                    pstr;
+  for (int idx = threadIdx.x; idx < G * HD; idx += kThreads) {
+    const int g = idx / HD;
+    const int d = idx % HD;
+    float m = neg_inf();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) m = fmaxf(m, sm_m[w][g]);
+    float s = 0.0f, o = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = sm_m[w][g];
+      const float c = (mw == neg_inf()) ? 0.0f : fast_exp2(mw - m);
+      s = fmaf(c, sm_s[w][g], s);
+      o = fmaf(c, sm_o[w][g][d], o);
+    }
+    float *rec = rec0 + (size_t)g * pstr;
+    rec[4 + d] = o;
+    if (d == 0) {
+      rec[0] = m * kLn2;  // -inf stays -inf
+      rec[1] = s;
+      rec[2] = __builtin_bit_cast(float, (int32_t)rg.lo);
+      rec[3] = __builtin_bit_cast(float, (int32_t)rg.hi);
+    }
+  }
+}
+
+}  // namespace detail
+
+// Launchers of the two kernel families (one per translation unit).
+hipError_t launch_partial_valu(int head_dim, int group, const PartialArgs &a,
+                               int batch, hipStream_t stream);
+hipError_t launch_partial_mfma(int head_dim, int group, const PartialArgs &a,
+                               int batch, hipStream_t stream);
+
+}  // namespace splitkv

@@ -1,0 +1,379 @@
+// splitkv_partial_mfma.hip -- partial kernel of split-KV grouped-query decode
+// attention for gfx950 (CDNA4), matrix-core form, used for head_dim 64, 128
+// and 256.
+//
+// Same contract as the vector-ALU kernel: one workgroup (4 waves) per (split,
+// KV head, sequence) on a static grid dim3(n_splits, n_kv_head, batch), the
+// live length read from positions[] on the device ("10 · R4 — decode
+// split-attention dim-parallel rewrite", section 2.2), all G query heads of
+// the KV head served by one read of each K/V row ("Red Lite dev35 —
+// long-context decode: grouped split-K attention", Change), online softmax per
+// head and one (mx, S, oc) record per query head ("10 · R4", section 2.1).
+//
+// Why matrix cores: grouping turns the scores of a row tile into a real dense
+// contraction, S[rows][heads] = K[rows][hd] · Q[heads][hd]ᵀ, and the output
+// update into O[hd][heads] += Vᵀ[hd][rows] · P[rows][heads]. Done with
+// vector FMAs these cost 2*G*hd FMAs per row plus the dot-product
+// reductions, which measured at about 78 wave instructions per KV row for
+// 28q/4kv hd128 (the VALU issue limit lands near half of the HBM rate). On
+// v_mfma_f32_16x16x32_f16 they take two MFMAs per 16 rows and 16 dims.
+//
+// Precision: the MFMA takes fp16 operands and accumulates in fp32. K and V
+// are fp16 already. q (scaled by scale*log2(e)) and the softmax weights p are
+// fp32; each is split into fp16 hi = fp16(x) and lo = fp16(x - hi), which
+// carry about 22 significant bits together. The 16 MFMA columns hold the G
+// heads' hi parts in columns 0..7 and their lo parts in columns 8..15, so one
+// MFMA computes both halves and a DPP row rotation by 8 adds them.
+//
+// Data flow of one wave over a tile of 32 rows (a workgroup's waves take
+// interleaved tiles; the next tile's loads are issued before the current tile
+// is computed):
+//   K: lane l loads 16 bytes of row (l % 16) at dims 32*ks + 8*(l/16): the
+//      A operand of S = K·Q'ᵀ directly (fp16, 16-byte coalesced loads);
+//   scores: D lane l holds rows 4*(l/16)+r of its column l % 16 -> max over
+//      the tile by in-lane max and two cross-group shuffles, p = exp2(s - m);
+//   p: already in the B-operand layout of O += Vᵀ·P (8 rows per lane);
+//   V: 16-byte coalesced loads, written row-major into the wave's LDS slice
+//      (rows padded by 32 bytes against bank conflicts), read back with the
+//      gfx950 transposing LDS read (ds_read_b64_tr_b16), which delivers four
+//      rows of one dim per lane: the A operand of Vᵀ·P.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "splitkv_internal.h"
+#include "splitkv_partial_common.h"
+
+namespace splitkv {
+namespace {
+
+using detail::dpp_mov;
+using detail::fast_exp2;
+using detail::kThreads;
+using detail::kWaves;
+using detail::neg_inf;
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef short short4v __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) short4v lds_short4v;
+
+constexpr int kTileRows = 32;
+constexpr int kRor8 = 0x128;  // DPP row_ror:8 (rotate by 8 within 16 lanes)
+
+template <int HD>
+struct MGeo {
+  static constexpr int KS = HD / 32;               // q·k k-steps of 32 dims
+  static constexpr int DB = HD / 16;               // p·v output blocks of 16 dims
+  static constexpr int LPR = HD / 8;               // lanes per row (V staging)
+  static constexpr int RPI = 64 / LPR;             // rows per staging load
+  static constexpr int NV = kTileRows / RPI;       // staging loads per tile
+  static constexpr int VSTR = HD * 2 + 32;         // LDS bytes per staged row
+  static constexpr int VTILE = kTileRows * VSTR;   // LDS bytes per wave
+  static constexpr bool kPrefetch = HD <= 128;     // two tiles in registers
+  static_assert(HD % 32 == 0 && HD <= 256, "head_dim");
+};
+
+template <int HD>
+struct TileRegs {
+  uint4 k[2][MGeo<HD>::KS];
+  uint4 v[MGeo<HD>::NV];
+};
+
+__device__ __forceinline__ half8 as_half8(const uint4 &u) {
+  return __builtin_bit_cast(half8, u);
+}
+
+// Order this wave's LDS accesses: a compiler barrier around the wave's own
+// in-order LDS traffic (the staged tile is private to the wave).
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Raw buffer view of one (sequence, KV head) slice of a cache: byte offsets
+// from its row 0, and a record limit at the split's end row, so every load of
+// a row at or past `hi` returns zeros in hardware (no predication, and rows
+// past the live length are never read from memory).
+struct CacheView {
+  __amdgpu_buffer_rsrc_t rsrc;
+};
+constexpr int kBufferWord3 = 0x00020000;  // gfx9-family raw buffer format
+
+__device__ __forceinline__ CacheView cache_view(const uint16_t *seq,
+                                                uint32_t limit_bytes) {
+  CacheView v;
+  v.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(seq),
+                                            (short)0, (int)limit_bytes,
+                                            kBufferWord3);
+  return v;
+}
+
+__device__ __forceinline__ uint4 load16(const CacheView &v, uint32_t off) {
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(v.rsrc, (int)off, 0, 0);
+  return make_uint4(x[0], x[1], x[2], x[3]);
+}
+
+// Issue the loads of one 32-row tile starting at row tb. koff / voff are the
+// lane's byte offsets within a row group; row_bytes = n_kv_head * HD * 2.
+template <int HD>
+__device__ __forceinline__ void load_tile(TileRegs<HD> &t, const CacheView &kv,
+                                          const CacheView &vv, uint32_t koff,
+                                          uint32_t voff, uint32_t row_bytes,
+                                          uint32_t tb) {
+  using Geo = MGeo<HD>;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    const uint32_t base = koff + (tb + 16u * rt) * row_bytes;
+#pragma unroll
+    for (int ks = 0; ks < Geo::KS; ++ks) t.k[rt][ks] = load16(kv, base + 64u * ks);
+  }
+#pragma unroll
+  for (int i = 0; i < Geo::NV; ++i)
+    t.v[i] = load16(vv, voff + (tb + (uint32_t)(Geo::RPI * i)) * row_bytes);
+}
+
+template <int HD>
+__device__ __forceinline__ void compute_tile(
+    const TileRegs<HD> &t, long long tb, long long hi,
+    const half8 (&qf)[MGeo<HD>::KS], float4v (&oacc)[MGeo<HD>::DB],
+    float &m_run, float &s_run, unsigned char *vlds, int col, int grp,
+    int lane, bool hi_col) {
+  using Geo = MGeo<HD>;
+  // a4: scores S = K · Q'ᵀ for the tile's two 16-row groups.
+  float4v sc[2];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+    sc[rt] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < Geo::KS; ++ks)
+      sc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(t.k[rt][ks]),
+                                                      qf[ks], sc[rt], 0, 0, 0);
+  }
+  // hi + lo columns; rows past the split's end score -inf.
+  float s[2][4];
+  float mt = neg_inf();
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float x = sc[rt][r] + dpp_mov<kRor8>(sc[rt][r]);
+      const long long row = tb + 16 * rt + 4 * grp + r;
+      s[rt][r] = row < hi ? x : neg_inf();
+      mt = fmaxf(mt, s[rt][r]);
+    }
+  }
+  mt = fmaxf(mt, __shfl_xor(mt, 16));
+  mt = fmaxf(mt, __shfl_xor(mt, 32));
+  // a5: online softmax. The tile's first row is live, so mn is finite.
+  const float mn = fmaxf(m_run, mt);
+  const float corr = fast_exp2(m_run - mn);  // 0 while m_run is -inf
+  half8 pf;
+  float psum = 0.0f;
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = fast_exp2(s[rt][r] - mn);  // exp2(-inf) = 0
+      psum += p;
+      const _Float16 h = (_Float16)p;
+      pf[4 * rt + r] = hi_col ? h : (_Float16)(p - (float)h);
+    }
+  }
+  s_run = s_run * corr + psum;
+  m_run = mn;
+#pragma unroll
+  for (int b = 0; b < Geo::DB; ++b) oacc[b] *= corr;
+
+  // V tile into this wave's LDS slice, row-major with padded rows.
+  wave_lds_fence();
+#pragma unroll
+  for (int i = 0; i < Geo::NV; ++i) {
+    const int rl = Geo::RPI * i + lane / Geo::LPR;
+    *reinterpret_cast<uint4 *>(vlds + rl * Geo::VSTR +
+                               16 * (lane % Geo::LPR)) = t.v[i];
+  }
+  wave_lds_fence();
+  // O += Vᵀ · P: lane (grp, col) reads dim 16b + col of rows 4*grp + 0..3
+  // and 16 + 4*grp + 0..3 (the same row order as its 8 p values).
+  const int c4 = col >> 2;
+  const int cm = col & 3;
+#pragma unroll
+  for (int b = 0; b < Geo::DB; ++b) {
+    const int byte_col = (16 * b + 4 * cm) * 2;
+    // address-space conversion of the generic LDS pointer (C-style cast)
+    lds_short4v *a0 =
+        (lds_short4v *)(vlds + (4 * grp + c4) * Geo::VSTR + byte_col);
+    lds_short4v *a1 =
+        (lds_short4v *)(vlds + (16 + 4 * grp + c4) * Geo::VSTR + byte_col);
+    const short4v r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(a0);
+    const short4v r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(a1);
+    const half8 vf = __builtin_shufflevector(__builtin_bit_cast(half4, r0),
+                                             __builtin_bit_cast(half4, r1), 0,
+                                             1, 2, 3, 4, 5, 6, 7);
+    oacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf, oacc[b], 0, 0, 0);
+  }
+}
+
+template <int HD, int G>
+__global__ __launch_bounds__(kThreads, HD >= 256 ? 1 : 2) void
+partial_mfma_kernel(PartialArgs a) {
+  using Geo = MGeo<HD>;
+  static_assert(G >= 1 && G <= 8, "group");
+  const int sp = blockIdx.x;
+  const int hk = blockIdx.y;
+  const int b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  const int col = lane & 15;
+  const int grp = lane >> 4;
+  const bool hi_col = col < 8;
+
+  __shared__ __attribute__((aligned(16))) unsigned char sm_v[kWaves * Geo::VTILE];
+  __shared__ float sm_m[kWaves][G];
+  __shared__ float sm_s[kWaves][G];
+  static_assert(sizeof(float) * kWaves * G * HD <= kWaves * Geo::VTILE,
+                "wave states alias the staging area");
+
+  // a1 + a2: live length and this split's rows.
+  const detail::SplitRange rg = detail::split_range(a, sp, b);
+  const long long lo = rg.lo;
+  const long long hi = rg.hi;
+
+  // a3: B operand of S = K·Q'ᵀ: column col holds head (col % 8), hi part in
+  // columns 0..7 and lo part in 8..15 (zero for heads past G), dims
+  // 32*ks + 8*grp + e, pre-scaled to base-2 units.
+  half8 qf[Geo::KS];
+  {
+    const int g = col & 7;
+    const float *qrow = a.q + ((size_t)b * a.n_head + (size_t)hk * G +
+                               (g < G ? g : 0)) * HD + 8 * grp;
+#pragma unroll
+    for (int ks = 0; ks < Geo::KS; ++ks) {
+      float x[8];
+      const float4 x0 = *reinterpret_cast<const float4 *>(qrow + 32 * ks);
+      const float4 x1 = *reinterpret_cast<const float4 *>(qrow + 32 * ks + 4);
+      x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
+      x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = (g < G) ? x[e] * a.scale_log2 : 0.0f;
+        const _Float16 h = (_Float16)v;
+        qf[ks][e] = hi_col ? h : (_Float16)(v - (float)h);
+      }
+    }
+  }
+
+  float4v oacc[Geo::DB];
+#pragma unroll
+  for (int i = 0; i < Geo::DB; ++i) oacc[i] = float4v{0.f, 0.f, 0.f, 0.f};
+  float m_run = neg_inf();
+  float s_run = 0.0f;
+
+  // Cache views of this (sequence, KV head): row r at byte r * row_bytes.
+  const uint32_t row_bytes = (uint32_t)(a.n_kv_head * HD * 2);
+  const size_t seq_base = ((size_t)b * (size_t)a.max_ctx * a.n_kv_head + hk) * HD;
+  const uint32_t limit = (uint32_t)hi * row_bytes;  // rows >= hi read as 0
+  const CacheView kv = cache_view(a.k + seq_base, limit);
+  const CacheView vv = cache_view(a.v + seq_base, limit);
+  const uint32_t koff = (uint32_t)col * row_bytes + 16u * grp;
+  const uint32_t voff = (uint32_t)(lane / Geo::LPR) * row_bytes +
+                        16u * (uint32_t)(lane % Geo::LPR);
+  unsigned char *vlds = sm_v + wave * Geo::VTILE;
+
+  // a4 + a5 over this wave's tiles. Double-buffered where the registers
+  // allow (head_dim <= 128): the next tile's loads are in flight while the
+  // current one is computed. At head_dim 256 one tile already holds 128 VGPRs
+  // of K/V and the occupancy is one wave per SIMD, so tiles go one at a time.
+  const long long step = (long long)kWaves * kTileRows;
+  long long t0 = lo + (long long)wave * kTileRows;
+  if constexpr (Geo::kPrefetch) {
+    TileRegs<HD> ta, tb;
+    if (t0 < hi) load_tile<HD>(ta, kv, vv, koff, voff, row_bytes, (uint32_t)t0);
+    while (t0 < hi) {
+      const long long t1 = t0 + step;
+      if (t1 < hi) load_tile<HD>(tb, kv, vv, koff, voff, row_bytes, (uint32_t)t1);
+      compute_tile<HD>(ta, t0, hi, qf, oacc, m_run, s_run, vlds, col, grp,
+                       lane, hi_col);
+      if (t1 >= hi) break;
+      const long long t2 = t1 + step;
+      if (t2 < hi) load_tile<HD>(ta, kv, vv, koff, voff, row_bytes, (uint32_t)t2);
+      compute_tile<HD>(tb, t1, hi, qf, oacc, m_run, s_run, vlds, col, grp,
+                       lane, hi_col);
+      t0 = t2;
+    }
+  } else {
+    for (; t0 < hi; t0 += step) {
+      TileRegs<HD> ta;
+      load_tile<HD>(ta, kv, vv, koff, voff, row_bytes, (uint32_t)t0);
+      compute_tile<HD>(ta, t0, hi, qf, oacc, m_run, s_run, vlds, col, grp,
+                       lane, hi_col);
+    }
+  }
+
+  // a6: wave state -> LDS (S over the four lane groups; O = hi + lo columns).
+  s_run += __shfl_xor(s_run, 16);
+  s_run += __shfl_xor(s_run, 32);
+  float4v o[Geo::DB];
+#pragma unroll
+  for (int i = 0; i < Geo::DB; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) o[i][r] = oacc[i][r] + dpp_mov<kRor8>(oacc[i][r]);
+  }
+  __syncthreads();  // every wave is done with its staging slice
+  float(&sm_o)[kWaves][G][HD] =
+      *reinterpret_cast<float(*)[kWaves][G][HD]>(sm_v);
+  if (col < G) {
+#pragma unroll
+    for (int i = 0; i < Geo::DB; ++i)
+      *reinterpret_cast<float4 *>(&sm_o[wave][col][16 * i + 4 * grp]) =
+          make_float4(o[i][0], o[i][1], o[i][2], o[i][3]);
+    if (grp == 0) {
+      sm_m[wave][col] = m_run;
+      sm_s[wave][col] = s_run;
+    }
+  }
+  __syncthreads();
+  detail::write_records<HD, G>(a, sp, hk, b, rg, sm_m, sm_s, sm_o);
+}
+
+template <int HD, int G>
+hipError_t launch_one(const PartialArgs &a, int batch, hipStream_t stream) {
+  hipLaunchKernelGGL((partial_mfma_kernel<HD, G>),
+                     dim3(a.n_splits, a.n_kv_head, batch), dim3(kThreads), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+template <int HD>
+hipError_t launch_hd(int group, const PartialArgs &a, int batch,
+                     hipStream_t stream) {
+  switch (group) {
+    case 1: return launch_one<HD, 1>(a, batch, stream);
+    case 2: return launch_one<HD, 2>(a, batch, stream);
+    case 3: return launch_one<HD, 3>(a, batch, stream);
+    case 4: return launch_one<HD, 4>(a, batch, stream);
+    case 5: return launch_one<HD, 5>(a, batch, stream);
+    case 6: return launch_one<HD, 6>(a, batch, stream);
+    case 7: return launch_one<HD, 7>(a, batch, stream);
+    case 8: return launch_one<HD, 8>(a, batch, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_partial_mfma(int head_dim, int group, const PartialArgs &a,
+                               int batch, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_hd<64>(group, a, batch, stream);
+    case 128: return launch_hd<128>(group, a, batch, stream);
+    case 256: return launch_hd<256>(group, a, batch, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace splitkv
