@@ -21,7 +21,9 @@ Reported (one JSON line on stdout):
 
 Usage: python bench.py [--steps K] [--warmup W] [--nkv N] [--layers L]
        python bench.py --sweep          # split-count sweep, one line per point
-       python bench.py --summarize-pmc DIR  # fold rocprofv3 --pmc output
+       python bench.py --mode kernels   # eager partial/combine launches + a copy
+       python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --kernels-json F
+                                        # fold two rocprofv3 --pmc runs
 """
 from __future__ import annotations
 
@@ -147,21 +149,38 @@ def time_replays(torch, graph, warmup: int, steps: int):
 
 
 def time_kernel(torch, launch, layers: int, reps: int):
-    """Average duration of one launch: events bracket each launch on the
-    stream it runs on, rotating over the layers' buffers."""
+    """Average duration of one launch of a kernel: `reps` launches rotating
+    over the layers' buffers are captured into one hipGraph (so host launch
+    cost is out of the picture) and the replays are timed with HIP events on
+    the replay stream. Returns (mean, best) milliseconds per launch over 5
+    replays. rocprofv3 --kernel-trace on --mode kernels times the same
+    launches."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for l in range(layers):
+            launch(l)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(reps):
+            launch(i % layers)
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    for l in range(layers):
-        launch(l)
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
-    for i in range(reps):
-        starts[i].record(stream)
-        launch(i % layers)
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return statistics.mean(ms), statistics.median(ms)
+    per = []
+    for _ in range(5):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        per.append(a.elapsed_time(b) / reps)
+    del g
+    return statistics.mean(per), min(per)
 
 
 def hbm_read_probe(torch, skv, gib: float = 4.0, reps: int = 5) -> float:
@@ -299,7 +318,7 @@ def run_main(args):
                      "kernel": "partial_kernel<128,7>",
                      "bytes_per_launch": kv_layer,
                      "avg_launch_us": round(p_mean * 1e3, 3),
-                     "median_launch_us": round(p_med * 1e3, 3),
+                     "best_batch_launch_us": round(p_med * 1e3, 3),
                      "traffic_source": traffic_src},
         "combine_avg_launch_us": round(c_mean * 1e3, 3),
         "hbm_read_probe_gbps": round(probe, 1) if probe else None,
@@ -327,10 +346,8 @@ def run_kernels(args):
         S, blk = skv.pick_splits(1, 28, 4, 128, max_ctx, cu)
     lay = Layers(args.layers, max_ctx, S, blk)
     lay.set_nkv(args.nkv)
-    for _ in range(args.steps):
-        for l in range(args.layers):
-            lay.partial(l)
-            lay.combine(l)
+    p_mean, _ = time_kernel(torch, lay.partial, args.layers, args.kernel_reps)
+    c_mean, _ = time_kernel(torch, lay.combine, args.layers, args.kernel_reps)
     nbytes = args.copy_mib << 20
     src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
     dst = torch.empty_like(src)
@@ -338,7 +355,10 @@ def run_kernels(args):
     torch.cuda.synchronize()
     print(json.dumps({"mode": "kernels", "nkv": args.nkv, "n_splits": S,
                       "block_len": blk, "layers": args.layers,
-                      "steps": args.steps, "copy_bytes": nbytes,
+                      "partial_launches": 6 * args.kernel_reps + args.layers,
+                      "partial_avg_us_events": round(p_mean * 1e3, 3),
+                      "combine_avg_us_events": round(c_mean * 1e3, 3),
+                      "copy_bytes": nbytes,
                       "kv_bytes_per_partial": synth.kv_bytes(4, 128, args.nkv),
                       "partial_src_sha256_16": source_hash()}), flush=True)
 
@@ -368,19 +388,54 @@ def run_sweep(args):
         torch.cuda.empty_cache()
 
 
-def summarize_pmc(directory: str, copy_bytes: int | None = None):
-    """Fold rocprofv3 --pmc counter CSVs into per-kernel means (KiB/dispatch)."""
-    rows = {}
-    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"),
-                          recursive=True):
-        with open(path) as f:
-            for r in csv.DictReader(f):
-                key = (r.get("Kernel_Name", "?"), r.get("Counter_Name", "?"))
-                rows.setdefault(key, []).append(float(r.get("Counter_Value", 0)))
-    out = {}
-    for (k, c), vals in sorted(rows.items()):
-        out.setdefault(k, {})[c] = {"mean": statistics.mean(vals), "n": len(vals)}
-    print(json.dumps(out, indent=1))
+def summarize_pmc(fetch_dir: str, write_dir: str, copy_bytes: int,
+                  kernels_json: str | None, out_path: str | None):
+    """Per-dispatch HBM traffic of the partial kernel from two rocprofv3 --pmc
+    runs of --mode kernels (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch),
+    each scaled by what the same counter reads for the plain copy kernel of
+    `copy_bytes` (which reads and writes exactly that many bytes)."""
+    def means(directory, counter):
+        vals = {}
+        for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"),
+                              recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    if r.get("Counter_Name") == counter:
+                        vals.setdefault(r["Kernel_Name"], []).append(
+                            float(r["Counter_Value"]))
+        return {k: statistics.mean(v) for k, v in vals.items()}
+
+    fetch = means(fetch_dir, "FETCH_SIZE")
+    write = means(write_dir, "WRITE_SIZE")
+
+    def pick(d, key):
+        ks = [k for k in d if key in k]
+        return d[ks[0]] if ks else None
+
+    f_copy, w_copy = pick(fetch, "probe_copy_kernel"), pick(write, "probe_copy_kernel")
+    f_part, w_part = pick(fetch, "partial_"), pick(write, "partial_")
+    f_comb, w_comb = pick(fetch, "combine_kernel"), pick(write, "combine_kernel")
+    f_scale = copy_bytes / (f_copy * 1024)
+    w_scale = copy_bytes / (w_copy * 1024)
+    res = {"fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+           "partial_fetch_bytes": round(f_part * 1024 * f_scale),
+           "partial_write_bytes": round(w_part * 1024 * w_scale),
+           "combine_fetch_bytes": round(f_comb * 1024 * f_scale),
+           "combine_write_bytes": round(w_comb * 1024 * w_scale)}
+    res["hbm_bytes_per_launch"] = res["partial_fetch_bytes"] + res["partial_write_bytes"]
+    if kernels_json:
+        with open(kernels_json) as f:
+            meta = json.loads(f.read().strip().splitlines()[-1])
+        for k in ("nkv", "n_splits", "block_len", "kv_bytes_per_partial",
+                  "partial_src_sha256_16"):
+            res[k] = meta[k]
+        res["fetch_over_algorithmic"] = round(
+            res["partial_fetch_bytes"] / meta["kv_bytes_per_partial"], 4)
+    print(json.dumps(res, indent=1))
+    if out_path:
+        with open(out_path, "w") as f:
+            json.dump(res, f, indent=1)
+            f.write("\n")
 
 
 def main():
@@ -394,7 +449,7 @@ def main():
                     default=[2048, 4096, 8192, 16384, 32768])
     ap.add_argument("--n-splits", type=int, default=0)
     ap.add_argument("--block-len", type=int, default=0)
-    ap.add_argument("--kernel-reps", type=int, default=112)
+    ap.add_argument("--kernel-reps", type=int, default=56)
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-probe", action="store_true")
@@ -402,12 +457,16 @@ def main():
     ap.add_argument("--sweep-splits", type=int, nargs="*",
                     default=[16, 32, 64, 128, 256, 512])
     ap.add_argument("--sweep-blocks", type=int, nargs="*", default=[128, 256, 512])
-    ap.add_argument("--summarize-pmc", default=None)
+    ap.add_argument("--summarize-pmc", nargs=2, default=None,
+                    metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--kernels-json", default=None)
+    ap.add_argument("--write-traffic", default=None)
     ap.add_argument("--mode", choices=["main", "kernels"], default="main")
     ap.add_argument("--copy-mib", type=int, default=256)
     args = ap.parse_args()
     if args.summarize_pmc:
-        summarize_pmc(args.summarize_pmc)
+        summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1],
+                      args.copy_mib << 20, args.kernels_json, args.write_traffic)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on one GPU only: this path has no multi-GPU "

@@ -13,7 +13,8 @@
 // 16-byte loads and NG = 256/C record groups run side by side; each thread
 // takes every NG-th record, several per pass with all loads issued before the
 // arithmetic, and keeps a running (max, sum, acc) with the same exact
-// re-weighting; the NG partial states are merged through LDS.
+// re-weighting. The NG partial states are merged by lane shuffles inside each
+// wave and through LDS across the four waves.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -94,30 +95,65 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
     m = mn;
   }
 
-  __shared__ float sm_m[NG];
-  __shared__ float sm_s[NG];
-  __shared__ float4 sm_acc[NG][C];
-  sm_acc[g0][c] = acc;
-  if (c == 0) {
-    sm_m[g0] = m;
-    sm_s[g0] = s;
+  // Merge the NG record groups: first across the groups of each wave with
+  // lane shuffles (groups are C lanes apart), then across the waves through
+  // LDS. Every lane of a group holds the same (m, s).
+#pragma unroll
+  for (int off = C; off < 64; off <<= 1) {
+    const float m2 = __shfl_xor(m, off);
+    const float s2 = __shfl_xor(s, off);
+    float4 a2;
+    a2.x = __shfl_xor(acc.x, off);
+    a2.y = __shfl_xor(acc.y, off);
+    a2.z = __shfl_xor(acc.z, off);
+    a2.w = __shfl_xor(acc.w, off);
+    const float mn = fmaxf(m, m2);
+    const float c1 = weight(m, mn);
+    const float c2 = weight(m2, mn);
+    s = s * c1 + s2 * c2;
+    acc.x = acc.x * c1 + a2.x * c2;
+    acc.y = acc.y * c1 + a2.y * c2;
+    acc.z = acc.z * c1 + a2.z * c2;
+    acc.w = acc.w * c1 + a2.w * c2;
+    m = mn;
+  }
+  constexpr int kW = kThreads / 64;
+  __shared__ float sm_m[kW];
+  __shared__ float sm_s[kW];
+  __shared__ float4 sm_acc[kW][C];
+  const int wave = tid >> 6;
+  const int lane = tid & 63;
+  if (lane < C) {
+    sm_acc[wave][lane] = acc;
+    if (lane == 0) {
+      sm_m[wave] = m;
+      sm_s[wave] = s;
+    }
   }
   __syncthreads();
-
-  for (int i = tid; i < DC; i += kThreads) {
+  if (tid < C) {
     float gm = neg_inf();
-    for (int g = 0; g < NG; ++g) gm = fmaxf(gm, sm_m[g]);
-    float st = 0.0f, o = 0.0f;
-    const int ci = i / 4, lane = i % 4;
-    for (int g = 0; g < NG; ++g) {
-      const float w = weight(sm_m[g], gm);
-      st = fmaf(w, sm_s[g], st);
-      const float4 v = sm_acc[g][ci];
-      const float x = lane == 0 ? v.x : lane == 1 ? v.y : lane == 2 ? v.z : v.w;
-      o = fmaf(w, x, o);
+#pragma unroll
+    for (int w = 0; w < kW; ++w) gm = fmaxf(gm, sm_m[w]);
+    float st = 0.0f;
+    float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int w = 0; w < kW; ++w) {
+      const float wt = weight(sm_m[w], gm);
+      st = fmaf(wt, sm_s[w], st);
+      const float4 x = sm_acc[w][tid];
+      o.x = fmaf(wt, x.x, o.x);
+      o.y = fmaf(wt, x.y, o.y);
+      o.z = fmaf(wt, x.z, o.z);
+      o.w = fmaf(wt, x.w, o.w);
     }
-    a.out[((size_t)b * a.n_head + h) * HD + d_base + i] =
-        (st > 0.0f) ? o / st : 0.0f;
+    float4 r;
+    r.x = (st > 0.0f) ? o.x / st : 0.0f;
+    r.y = (st > 0.0f) ? o.y / st : 0.0f;
+    r.z = (st > 0.0f) ? o.z / st : 0.0f;
+    r.w = (st > 0.0f) ? o.w / st : 0.0f;
+    *reinterpret_cast<float4 *>(
+        &a.out[((size_t)b * a.n_head + h) * HD + d_base + 4 * tid]) = r;
   }
 }
 

@@ -100,6 +100,8 @@ struct CacheView {
   __amdgpu_buffer_rsrc_t rsrc;
 };
 constexpr int kBufferWord3 = 0x00020000;  // gfx9-family raw buffer format
+// Cache policy of the K/V loads: non-temporal (each byte is read once).
+constexpr int kLoadNT = 2;
 
 __device__ __forceinline__ CacheView cache_view(const uint16_t *seq,
                                                 uint32_t limit_bytes) {
@@ -112,7 +114,8 @@ __device__ __forceinline__ CacheView cache_view(const uint16_t *seq,
 
 __device__ __forceinline__ uint4 load16(const CacheView &v, uint32_t off) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(v.rsrc, (int)off, 0, 0);
+  const u32x4 x =
+      __builtin_amdgcn_raw_buffer_load_b128(v.rsrc, (int)off, 0, kLoadNT);
   return make_uint4(x[0], x[1], x[2], x[3]);
 }
 
@@ -314,30 +317,68 @@ partial_mfma_kernel(PartialArgs a) {
     }
   }
 
-  // a6: wave state -> LDS (S over the four lane groups; O = hi + lo columns).
+  // a6: merge the four waves and write the records.
+  // (1) each wave's sum over its four lane groups, (max, sum) to LDS;
   s_run += __shfl_xor(s_run, 16);
   s_run += __shfl_xor(s_run, 32);
-  float4v o[Geo::DB];
-#pragma unroll
-  for (int i = 0; i < Geo::DB; ++i) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) o[i][r] = oacc[i][r] + dpp_mov<kRor8>(oacc[i][r]);
+  if (grp == 0 && col < G) {
+    sm_m[wave][col] = m_run;
+    sm_s[wave][col] = s_run;
   }
-  __syncthreads();  // every wave is done with its staging slice
+  __syncthreads();  // also: every wave is done with its staging slice
+  // (2) each lane rescales its own O columns by exp2(m_wave - m_all) and adds
+  // the hi and lo columns; the scaled O goes to LDS (over the staging area);
+  const int g = col & 7;
+  float m_all = neg_inf();
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w)
+    m_all = fmaxf(m_all, sm_m[w][g < G ? g : 0]);
+  const float c_self = (m_run == neg_inf()) ? 0.0f : fast_exp2(m_run - m_all);
   float(&sm_o)[kWaves][G][HD] =
       *reinterpret_cast<float(*)[kWaves][G][HD]>(sm_v);
-  if (col < G) {
 #pragma unroll
-    for (int i = 0; i < Geo::DB; ++i)
+  for (int i = 0; i < Geo::DB; ++i) {
+    float o4[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      o4[r] = (oacc[i][r] + dpp_mov<kRor8>(oacc[i][r])) * c_self;
+    if (col < G)
       *reinterpret_cast<float4 *>(&sm_o[wave][col][16 * i + 4 * grp]) =
-          make_float4(o[i][0], o[i][1], o[i][2], o[i][3]);
-    if (grp == 0) {
-      sm_m[wave][col] = m_run;
-      sm_s[wave][col] = s_run;
-    }
+          make_float4(o4[0], o4[1], o4[2], o4[3]);
   }
   __syncthreads();
-  detail::write_records<HD, G>(a, sp, hk, b, rg, sm_m, sm_s, sm_o);
+  // (3) records: one float4 of oc per thread and step, header by d4 == 0.
+  constexpr int D4 = HD / 4;
+  const size_t pstr = 4 + HD;
+  float *rec0 = a.partials +
+                (((size_t)b * a.n_splits + sp) * a.n_head + (size_t)hk * G) *
+                    pstr;
+  for (int idx = tid; idx < G * D4; idx += kThreads) {
+    const int gg = idx / D4;
+    const int d4 = idx % D4;
+    float4 acc = *reinterpret_cast<const float4 *>(&sm_o[0][gg][4 * d4]);
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) {
+      const float4 x = *reinterpret_cast<const float4 *>(&sm_o[w][gg][4 * d4]);
+      acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+    }
+    float *rec = rec0 + (size_t)gg * pstr;
+    *reinterpret_cast<float4 *>(rec + 4 + 4 * d4) = acc;
+    if (d4 == 0) {
+      float mm = neg_inf();
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, sm_m[w][gg]);
+      float st = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float mw = sm_m[w][gg];
+        st += (mw == neg_inf()) ? 0.0f : fast_exp2(mw - mm) * sm_s[w][gg];
+      }
+      *reinterpret_cast<float4 *>(rec) = make_float4(
+          mm * detail::kLn2, st, __builtin_bit_cast(float, (int32_t)rg.lo),
+          __builtin_bit_cast(float, (int32_t)rg.hi));
+    }
+  }
 }
 
 template <int HD, int G>
