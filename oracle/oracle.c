@@ -18,8 +18,8 @@
  *
  * Readings of points the pages leave open (each is restated where it is used):
  *   - query head h reads KV head h / G with G = n_head / n_kv_head (contiguous
- *     groups; [R4] 3.2 uses an undefined `hk`, [RL35] Finding speaks of "the
- *     8 query heads sharing a KV head");
+ *     groups; [R4] 3.2 uses an undefined `hk`, and [RL35] Finding describes
+ *     groups of consecutive query heads served by one KV head);
  *   - the cache row of position p, KV head g starts at element
  *     ((b*max_ctx + p)*n_kv_head + g)*head_dim ([R4] 3.2 addresses rows as
  *     `pos*stride_kv + hk*hd`; stride_kv is read as n_kv_head*head_dim);
