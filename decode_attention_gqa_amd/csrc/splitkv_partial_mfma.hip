@@ -92,55 +92,73 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Raw buffer view of one (sequence, KV head) slice of a cache: byte offsets
-// from its row 0, and a record limit at the split's end row, so every load of
-// a row at or past `hi` returns zeros in hardware (no predication, and rows
-// past the live length are never read from memory).
-struct CacheView {
-  __amdgpu_buffer_rsrc_t rsrc;
-};
 constexpr int kBufferWord3 = 0x00020000;  // gfx9-family raw buffer format
 // Cache policy of the K/V loads: non-temporal (each byte is read once).
 constexpr int kLoadNT = 2;
 
-__device__ __forceinline__ CacheView cache_view(const uint16_t *seq,
-                                                uint32_t limit_bytes) {
-  CacheView v;
-  v.rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t *>(seq),
-                                            (short)0, (int)limit_bytes,
-                                            kBufferWord3);
-  return v;
-}
-
-__device__ __forceinline__ uint4 load16(const CacheView &v, uint32_t off) {
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-  const u32x4 x =
-      __builtin_amdgcn_raw_buffer_load_b128(v.rsrc, (int)off, 0, kLoadNT);
+  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, kLoadNT);
   return make_uint4(x[0], x[1], x[2], x[3]);
 }
 
-// Issue the loads of one 32-row tile starting at row tb. koff / voff are the
-// lane's byte offsets within a row group; row_bytes = n_kv_head * HD * 2.
+// Per-lane byte offsets of the loads, the same for every row group: K lane l
+// reads row l % 16 of its 16-row group at dims 8*(l/16) (+ 32*ks dims through
+// the instruction offset); V lane l reads row l / LPR of its RPI-row group at
+// dims 8*(l % LPR). row_bytes = n_kv_head * HD * 2.
+struct LaneOffsets {
+  uint32_t k;
+  uint32_t v;
+};
+
 template <int HD>
-__device__ __forceinline__ void load_tile(TileRegs<HD> &t, const CacheView &kv,
-                                          const CacheView &vv, uint32_t koff,
-                                          uint32_t voff, uint32_t row_bytes,
-                                          uint32_t tb) {
+__device__ __forceinline__ LaneOffsets lane_offsets(uint32_t row_bytes,
+                                                    int col, int grp,
+                                                    int lane) {
+  using Geo = MGeo<HD>;
+  LaneOffsets o;
+  o.k = (uint32_t)col * row_bytes + 16u * grp;
+  o.v = (uint32_t)(lane / Geo::LPR) * row_bytes +
+        16u * (uint32_t)(lane % Geo::LPR);
+  return o;
+}
+
+// Raw buffer view of rows [first, hi) of one (sequence, KV head) cache slice:
+// based at row `first`, record limit at row hi, so loads of rows at or past hi
+// return zeros in hardware and are never fetched. Base and limit are
+// wave-uniform (scalar registers).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_view(
+    const uint16_t *seq, uint32_t row_bytes, uint32_t first, uint32_t hi) {
+  const int limit = first < hi ? (int)((hi - first) * row_bytes) : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t *>(seq + (size_t)first * (row_bytes / 2)), (short)0,
+      limit, kBufferWord3);
+}
+
+// Issue the loads of the 32-row tile starting at row tb (tb < hi).
+template <int HD>
+__device__ __forceinline__ void load_tile(TileRegs<HD> &t, const uint16_t *kseq,
+                                          const uint16_t *vseq,
+                                          uint32_t row_bytes, uint32_t tb,
+                                          uint32_t hi, const LaneOffsets &o) {
   using Geo = MGeo<HD>;
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
-    const uint32_t base = koff + (tb + 16u * rt) * row_bytes;
+    const __amdgpu_buffer_rsrc_t r = rows_view(kseq, row_bytes, tb + 16u * rt, hi);
 #pragma unroll
-    for (int ks = 0; ks < Geo::KS; ++ks) t.k[rt][ks] = load16(kv, base + 64u * ks);
+    for (int ks = 0; ks < Geo::KS; ++ks) t.k[rt][ks] = load16(r, o.k + 64u * ks);
   }
 #pragma unroll
-  for (int i = 0; i < Geo::NV; ++i)
-    t.v[i] = load16(vv, voff + (tb + (uint32_t)(Geo::RPI * i)) * row_bytes);
+  for (int i = 0; i < Geo::NV; ++i) {
+    const __amdgpu_buffer_rsrc_t r =
+        rows_view(vseq, row_bytes, tb + (uint32_t)(Geo::RPI * i), hi);
+    t.v[i] = load16(r, o.v);
+  }
 }
 
 template <int HD>
 __device__ __forceinline__ void compute_tile(
-    const TileRegs<HD> &t, long long tb, long long hi,
+    const TileRegs<HD> &t, uint32_t tb, uint32_t hi,
     const half8 (&qf)[MGeo<HD>::KS], float4v (&oacc)[MGeo<HD>::DB],
     float &m_run, float &s_run, unsigned char *vlds, int col, int grp,
     int lane, bool hi_col) {
@@ -155,18 +173,26 @@ __device__ __forceinline__ void compute_tile(
       sc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(t.k[rt][ks]),
                                                       qf[ks], sc[rt], 0, 0, 0);
   }
-  // hi + lo columns; rows past the split's end score -inf.
+  // hi + lo columns; rows past the split's end (last tile only) score -inf.
   float s[2][4];
+#pragma unroll
+  for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) s[rt][r] = sc[rt][r] + dpp_mov<kRor8>(sc[rt][r]);
+  }
+  if (tb + kTileRows > hi) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (tb + (uint32_t)(16 * rt + 4 * grp + r) >= hi) s[rt][r] = neg_inf();
+    }
+  }
   float mt = neg_inf();
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float x = sc[rt][r] + dpp_mov<kRor8>(sc[rt][r]);
-      const long long row = tb + 16 * rt + 4 * grp + r;
-      s[rt][r] = row < hi ? x : neg_inf();
-      mt = fmaxf(mt, s[rt][r]);
-    }
+    for (int r = 0; r < 4; ++r) mt = fmaxf(mt, s[rt][r]);
   }
   mt = fmaxf(mt, __shfl_xor(mt, 16));
   mt = fmaxf(mt, __shfl_xor(mt, 32));
@@ -185,10 +211,15 @@ __device__ __forceinline__ void compute_tile(
       pf[4 * rt + r] = hi_col ? h : (_Float16)(p - (float)h);
     }
   }
-  s_run = s_run * corr + psum;
-  m_run = mn;
+  // Rescale only when some column's running max moved (else corr is 1 for
+  // every column and the products would change nothing).
+  if (__any(mn != m_run)) {
+    s_run *= corr;
 #pragma unroll
-  for (int b = 0; b < Geo::DB; ++b) oacc[b] *= corr;
+    for (int b = 0; b < Geo::DB; ++b) oacc[b] *= corr;
+  }
+  s_run += psum;
+  m_run = mn;
 
   // V tile into this wave's LDS slice, row-major with padded rows.
   wave_lds_fence();
@@ -229,7 +260,8 @@ partial_mfma_kernel(PartialArgs a) {
   const int hk = blockIdx.y;
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  // wave index, provably uniform (scalar) so per-tile row math stays scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int col = lane & 15;
   const int grp = lane >> 4;
@@ -238,37 +270,24 @@ partial_mfma_kernel(PartialArgs a) {
   __shared__ __attribute__((aligned(16))) unsigned char sm_v[kWaves * Geo::VTILE];
   __shared__ float sm_m[kWaves][G];
   __shared__ float sm_s[kWaves][G];
-  static_assert(sizeof(float) * kWaves * G * HD <= kWaves * Geo::VTILE,
-                "wave states alias the staging area");
+  __shared__ __attribute__((aligned(16))) float sm_o[kWaves][G][HD];
 
   // a1 + a2: live length and this split's rows.
   const detail::SplitRange rg = detail::split_range(a, sp, b);
   const long long lo = rg.lo;
   const long long hi = rg.hi;
 
-  // a3: B operand of S = K·Q'ᵀ: column col holds head (col % 8), hi part in
-  // columns 0..7 and lo part in 8..15 (zero for heads past G), dims
-  // 32*ks + 8*grp + e, pre-scaled to base-2 units.
-  half8 qf[Geo::KS];
-  {
-    const int g = col & 7;
-    const float *qrow = a.q + ((size_t)b * a.n_head + (size_t)hk * G +
-                               (g < G ? g : 0)) * HD + 8 * grp;
-#pragma unroll
-    for (int ks = 0; ks < Geo::KS; ++ks) {
-      float x[8];
-      const float4 x0 = *reinterpret_cast<const float4 *>(qrow + 32 * ks);
-      const float4 x1 = *reinterpret_cast<const float4 *>(qrow + 32 * ks + 4);
-      x[0] = x0.x; x[1] = x0.y; x[2] = x0.z; x[3] = x0.w;
-      x[4] = x1.x; x[5] = x1.y; x[6] = x1.z; x[7] = x1.w;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v = (g < G) ? x[e] * a.scale_log2 : 0.0f;
-        const _Float16 h = (_Float16)v;
-        qf[ks][e] = hi_col ? h : (_Float16)(v - (float)h);
-      }
-    }
-  }
+  // This (sequence, KV head) slice of the caches: row r at byte r * row_bytes.
+  const uint32_t row_bytes = (uint32_t)(a.n_kv_head * HD * 2);
+  const size_t seq_base = ((size_t)b * (size_t)a.max_ctx * a.n_kv_head + hk) * HD;
+  const uint16_t *kseq = a.k + seq_base;
+  const uint16_t *vseq = a.v + seq_base;
+  const LaneOffsets lo_off = lane_offsets<HD>(row_bytes, col, grp, lane);
+  unsigned char *vlds = sm_v + wave * Geo::VTILE;
+  const uint32_t hi32 = (uint32_t)hi;
+  const uint32_t step = (uint32_t)(kWaves * kTileRows);
+  uint32_t t0 = (uint32_t)lo + (uint32_t)(wave * kTileRows);
+  if (lo >= hi) t0 = hi32;  // idle split
 
   float4v oacc[Geo::DB];
 #pragma unroll
@@ -276,78 +295,99 @@ partial_mfma_kernel(PartialArgs a) {
   float m_run = neg_inf();
   float s_run = 0.0f;
 
-  // Cache views of this (sequence, KV head): row r at byte r * row_bytes.
-  const uint32_t row_bytes = (uint32_t)(a.n_kv_head * HD * 2);
-  const size_t seq_base = ((size_t)b * (size_t)a.max_ctx * a.n_kv_head + hk) * HD;
-  const uint32_t limit = (uint32_t)hi * row_bytes;  // rows >= hi read as 0
-  const CacheView kv = cache_view(a.k + seq_base, limit);
-  const CacheView vv = cache_view(a.v + seq_base, limit);
-  const uint32_t koff = (uint32_t)col * row_bytes + 16u * grp;
-  const uint32_t voff = (uint32_t)(lane / Geo::LPR) * row_bytes +
-                        16u * (uint32_t)(lane % Geo::LPR);
-  unsigned char *vlds = sm_v + wave * Geo::VTILE;
-
-  // a4 + a5 over this wave's tiles. Double-buffered where the registers
-  // allow (head_dim <= 128): the next tile's loads are in flight while the
-  // current one is computed. At head_dim 256 one tile already holds 128 VGPRs
-  // of K/V and the occupancy is one wave per SIMD, so tiles go one at a time.
-  const long long step = (long long)kWaves * kTileRows;
-  long long t0 = lo + (long long)wave * kTileRows;
-  if constexpr (Geo::kPrefetch) {
+  // A wave whose first tile starts at or past hi has no rows: it keeps the
+  // empty state (-inf, 0, 0) and issues no loads at all.
+  if (t0 < hi32) {
+    // Issue order: first tile's K/V, then the queries, then the second tile.
+    // The first K/V requests must not wait behind the query conversion, whose
+    // loads queue behind the other waves' streaming traffic; converting the
+    // queries waits only for the loads issued before them. The second tile's
+    // loads are issued unconditionally: a tile at or past hi has a zero record
+    // limit, so its loads return zeros without touching memory, and the wait
+    // counts stay exact.
     TileRegs<HD> ta, tb;
-    if (t0 < hi) load_tile<HD>(ta, kv, vv, koff, voff, row_bytes, (uint32_t)t0);
-    while (t0 < hi) {
-      const long long t1 = t0 + step;
-      if (t1 < hi) load_tile<HD>(tb, kv, vv, koff, voff, row_bytes, (uint32_t)t1);
-      compute_tile<HD>(ta, t0, hi, qf, oacc, m_run, s_run, vlds, col, grp,
-                       lane, hi_col);
-      if (t1 >= hi) break;
-      const long long t2 = t1 + step;
-      if (t2 < hi) load_tile<HD>(ta, kv, vv, koff, voff, row_bytes, (uint32_t)t2);
-      compute_tile<HD>(tb, t1, hi, qf, oacc, m_run, s_run, vlds, col, grp,
-                       lane, hi_col);
-      t0 = t2;
+    load_tile<HD>(ta, kseq, vseq, row_bytes, t0, hi32, lo_off);
+
+    // a3: B operand of S = K·Q'ᵀ: column col holds head (col % 8), hi part in
+    // columns 0..7 and lo part in 8..15 (zero for heads past G), dims
+    // 32*ks + 8*grp + e, pre-scaled to base-2 units.
+    const int gq = col & 7;
+    float4 qraw[Geo::KS][2];
+    {
+      const float *qrow = a.q + ((size_t)b * a.n_head + (size_t)hk * G +
+                                 (gq < G ? gq : 0)) * HD + 8 * grp;
+#pragma unroll
+      for (int ks = 0; ks < Geo::KS; ++ks) {
+        qraw[ks][0] = *reinterpret_cast<const float4 *>(qrow + 32 * ks);
+        qraw[ks][1] = *reinterpret_cast<const float4 *>(qrow + 32 * ks + 4);
+      }
     }
-  } else {
-    for (; t0 < hi; t0 += step) {
-      TileRegs<HD> ta;
-      load_tile<HD>(ta, kv, vv, koff, voff, row_bytes, (uint32_t)t0);
-      compute_tile<HD>(ta, t0, hi, qf, oacc, m_run, s_run, vlds, col, grp,
-                       lane, hi_col);
+    if constexpr (Geo::kPrefetch)
+      load_tile<HD>(tb, kseq, vseq, row_bytes, t0 + step, hi32, lo_off);
+    half8 qf[Geo::KS];
+#pragma unroll
+    for (int ks = 0; ks < Geo::KS; ++ks) {
+      const float x[8] = {qraw[ks][0].x, qraw[ks][0].y, qraw[ks][0].z,
+                          qraw[ks][0].w, qraw[ks][1].x, qraw[ks][1].y,
+                          qraw[ks][1].z, qraw[ks][1].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float v = (gq < G) ? x[e] * a.scale_log2 : 0.0f;
+        const _Float16 h = (_Float16)v;
+        qf[ks][e] = hi_col ? h : (_Float16)(v - (float)h);
+      }
+    }
+
+    // a4 + a5 over this wave's tiles. Double-buffered where the registers
+    // allow (head_dim <= 128): two tiles are always in flight, the one being
+    // computed and the next. At head_dim 256 one tile already holds 128 VGPRs
+    // of K/V and the occupancy is one wave per SIMD, so tiles go one at a
+    // time.
+    if constexpr (Geo::kPrefetch) {
+      // invariant: ta holds tile t0, tb holds tile t0 + step
+      while (true) {
+        const uint32_t t1 = t0 + step;
+        compute_tile<HD>(ta, t0, hi32, qf, oacc, m_run, s_run, vlds, col, grp,
+                         lane, hi_col);
+        if (t1 >= hi32) break;
+        load_tile<HD>(ta, kseq, vseq, row_bytes, t1 + step, hi32, lo_off);
+        compute_tile<HD>(tb, t1, hi32, qf, oacc, m_run, s_run, vlds, col, grp,
+                         lane, hi_col);
+        t0 = t1 + step;
+        if (t0 >= hi32) break;
+        load_tile<HD>(tb, kseq, vseq, row_bytes, t0 + step, hi32, lo_off);
+      }
+    } else {
+      while (true) {
+        compute_tile<HD>(ta, t0, hi32, qf, oacc, m_run, s_run, vlds, col, grp,
+                         lane, hi_col);
+        t0 += step;
+        if (t0 >= hi32) break;
+        load_tile<HD>(ta, kseq, vseq, row_bytes, t0, hi32, lo_off);
+      }
     }
   }
 
-  // a6: merge the four waves and write the records.
-  // (1) each wave's sum over its four lane groups, (max, sum) to LDS;
+  // a6: merge the four waves and write the records. Each wave puts its state
+  // in LDS (max and sum per head; O with the hi and lo columns added), then
+  // after one barrier every thread merges one float4 of one head's output
+  // over the four waves with exact weights exp2(m_wave - m_all).
   s_run += __shfl_xor(s_run, 16);
   s_run += __shfl_xor(s_run, 32);
   if (grp == 0 && col < G) {
     sm_m[wave][col] = m_run;
     sm_s[wave][col] = s_run;
   }
-  __syncthreads();  // also: every wave is done with its staging slice
-  // (2) each lane rescales its own O columns by exp2(m_wave - m_all) and adds
-  // the hi and lo columns; the scaled O goes to LDS (over the staging area);
-  const int g = col & 7;
-  float m_all = neg_inf();
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w)
-    m_all = fmaxf(m_all, sm_m[w][g < G ? g : 0]);
-  const float c_self = (m_run == neg_inf()) ? 0.0f : fast_exp2(m_run - m_all);
-  float(&sm_o)[kWaves][G][HD] =
-      *reinterpret_cast<float(*)[kWaves][G][HD]>(sm_v);
 #pragma unroll
   for (int i = 0; i < Geo::DB; ++i) {
     float o4[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-      o4[r] = (oacc[i][r] + dpp_mov<kRor8>(oacc[i][r])) * c_self;
+    for (int r = 0; r < 4; ++r) o4[r] = oacc[i][r] + dpp_mov<kRor8>(oacc[i][r]);
     if (col < G)
       *reinterpret_cast<float4 *>(&sm_o[wave][col][16 * i + 4 * grp]) =
           make_float4(o4[0], o4[1], o4[2], o4[3]);
   }
   __syncthreads();
-  // (3) records: one float4 of oc per thread and step, header by d4 == 0.
   constexpr int D4 = HD / 4;
   const size_t pstr = 4 + HD;
   float *rec0 = a.partials +
@@ -356,28 +396,28 @@ partial_mfma_kernel(PartialArgs a) {
   for (int idx = tid; idx < G * D4; idx += kThreads) {
     const int gg = idx / D4;
     const int d4 = idx % D4;
-    float4 acc = *reinterpret_cast<const float4 *>(&sm_o[0][gg][4 * d4]);
+    float mm = neg_inf();
 #pragma unroll
-    for (int w = 1; w < kWaves; ++w) {
+    for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, sm_m[w][gg]);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float st = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = sm_m[w][gg];
+      const float c = (mw == neg_inf()) ? 0.0f : fast_exp2(mw - mm);
       const float4 x = *reinterpret_cast<const float4 *>(&sm_o[w][gg][4 * d4]);
-      acc.x += x.x; acc.y += x.y; acc.z += x.z; acc.w += x.w;
+      acc.x = fmaf(c, x.x, acc.x);
+      acc.y = fmaf(c, x.y, acc.y);
+      acc.z = fmaf(c, x.z, acc.z);
+      acc.w = fmaf(c, x.w, acc.w);
+      st = fmaf(c, sm_s[w][gg], st);
     }
     float *rec = rec0 + (size_t)gg * pstr;
     *reinterpret_cast<float4 *>(rec + 4 + 4 * d4) = acc;
-    if (d4 == 0) {
-      float mm = neg_inf();
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, sm_m[w][gg]);
-      float st = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) {
-        const float mw = sm_m[w][gg];
-        st += (mw == neg_inf()) ? 0.0f : fast_exp2(mw - mm) * sm_s[w][gg];
-      }
+    if (d4 == 0)
       *reinterpret_cast<float4 *>(rec) = make_float4(
           mm * detail::kLn2, st, __builtin_bit_cast(float, (int32_t)rg.lo),
           __builtin_bit_cast(float, (int32_t)rg.hi));
-    }
   }
 }
 
