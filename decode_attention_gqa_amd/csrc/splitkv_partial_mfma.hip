@@ -304,7 +304,8 @@ partial_mfma_kernel(PartialArgs a) {
     // queries waits only for the loads issued before them. The second tile's
     // loads are issued unconditionally: a tile at or past hi has a zero record
     // limit, so its loads return zeros without touching memory, and the wait
-    // counts stay exact.
+    // before the query conversion stays exact (a conditional load between
+    // the query loads and their use makes the compiler wait for it too).
     TileRegs<HD> ta, tb;
     load_tile<HD>(ta, kseq, vseq, row_bytes, t0, hi32, lo_off);
 
@@ -350,12 +351,17 @@ partial_mfma_kernel(PartialArgs a) {
         compute_tile<HD>(ta, t0, hi32, qf, oacc, m_run, s_run, vlds, col, grp,
                          lane, hi_col);
         if (t1 >= hi32) break;
-        load_tile<HD>(ta, kseq, vseq, row_bytes, t1 + step, hi32, lo_off);
+        // Inside the loop the next tile is loaded only if it has rows: even
+        // zero-limit loads cost address-unit time, and a wave often has just
+        // a few tiles.
+        if (t1 + step < hi32)
+          load_tile<HD>(ta, kseq, vseq, row_bytes, t1 + step, hi32, lo_off);
         compute_tile<HD>(tb, t1, hi32, qf, oacc, m_run, s_run, vlds, col, grp,
                          lane, hi_col);
         t0 = t1 + step;
         if (t0 >= hi32) break;
-        load_tile<HD>(tb, kseq, vseq, row_bytes, t0 + step, hi32, lo_off);
+        if (t0 + step < hi32)
+          load_tile<HD>(tb, kseq, vseq, row_bytes, t0 + step, hi32, lo_off);
       }
     } else {
       while (true) {
