@@ -29,6 +29,7 @@ from __future__ import annotations
 
 import argparse
 import csv
+import dataclasses
 import glob
 import hashlib
 import json
@@ -363,6 +364,59 @@ def run_kernels(args):
                       "partial_src_sha256_16": source_hash()}), flush=True)
 
 
+def run_ragged(args):
+    """Ragged batch: 32 sequences, 32q/8kv hd128, nkv_b ~ U{512..32768}; one
+    graph of partial + combine per (n_splits, block_len) point; prints one JSON
+    line per point (KV GB/s over the live rows of all sequences)."""
+    import numpy as np
+    import torch
+
+    import decode_attention_gqa_amd as skv
+    import synth
+    sh = synth.CFG5
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    lengths = synth.cfg5_lengths()[:args.ragged_batch]
+    if args.ragged_full:
+        lengths[:] = sh.max_ctx
+    sh = dataclasses.replace(sh, batch=len(lengths))
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    # K/V values do not affect timing: drawn on the GPU (seeded) for speed
+    k = torch.randn((sh.batch, sh.max_ctx, sh.n_kv_head, sh.head_dim),
+                    generator=g, device=dev, dtype=torch.float16)
+    v = torch.randn(k.shape, generator=g, device=dev, dtype=torch.float16)
+    q = torch.from_numpy(synth.make_q(5, 0, sh)).to(dev)
+    pos = torch.from_numpy((lengths - 1).astype(np.int32)).to(dev)
+    kv = synth.kv_bytes(sh.n_kv_head, sh.head_dim, lengths)
+    out = torch.empty((sh.batch, sh.n_head, sh.head_dim), device=dev)
+    S_h, blk_h = skv.pick_splits(sh.batch, sh.n_head, sh.n_kv_head, sh.head_dim,
+                                 sh.max_ctx, cu)
+    points = [(S_h, blk_h)] + [(s, 0) for s in args.sweep_splits] + \
+             [(-(-sh.max_ctx // b), b) for b in args.sweep_blocks]
+    for S, blk in points:
+        part = torch.empty(skv.partials_bytes(sh.batch, sh.n_head, sh.head_dim, S)
+                           // 4, device=dev)
+
+        def step():
+            skv.decode_attn(q, k, v, pos, part, out, S, blk, sh.scale)
+        step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        per, total, _ = time_replays(torch, graph, args.warmup, args.steps)
+        med = statistics.median(per)
+        print(json.dumps({"ragged": not args.ragged_full, "batch": sh.batch,
+                          "n_splits": S, "block_len": blk,
+                          "heuristic": (S, blk) == (S_h, blk_h),
+                          "kv_bytes": kv, "ms_per_step": round(med, 4),
+                          "kv_gbps": round(kv / (med * 1e-3) / 1e9, 1)}),
+              flush=True)
+        del graph, part
+        torch.cuda.empty_cache()
+
+
 def run_sweep(args):
     import torch
 
@@ -461,7 +515,11 @@ def main():
                     metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--kernels-json", default=None)
     ap.add_argument("--write-traffic", default=None)
-    ap.add_argument("--mode", choices=["main", "kernels"], default="main")
+    ap.add_argument("--mode", choices=["main", "kernels", "ragged"],
+                    default="main")
+    ap.add_argument("--ragged-batch", type=int, default=32)
+    ap.add_argument("--ragged-full", action="store_true",
+                    help="every sequence at full length (uniform batch)")
     ap.add_argument("--copy-mib", type=int, default=256)
     args = ap.parse_args()
     if args.summarize_pmc:
@@ -477,6 +535,8 @@ def main():
         run_sweep(args)
     elif args.mode == "kernels":
         run_kernels(args)
+    elif args.mode == "ragged":
+        run_ragged(args)
     else:
         run_main(args)
     return 0

@@ -145,10 +145,18 @@ int splitkv_pick_splits(int batch, int n_head, int n_kv_head, int head_dim,
       check_shape(batch, n_head, n_kv_head, head_dim, max_ctx, 1, 0);
   if (st != SPLITKV_OK) return st;
   const int group = n_head / n_kv_head;
-  // Enough workgroups for two per compute unit over the whole grid ...
   const long long units = (long long)batch * n_kv_head;
-  const long long target = 2LL * cu_count;
-  long long s = (target + units - 1) / units;
+  // One full round of resident workgroups (two per compute unit). With one
+  // sequence every split has the same work, so a single round is best.
+  long long s = (2LL * cu_count + units - 1) / units;
+  // With several sequences the lengths can differ and the host does not see
+  // them: about 16 workgroups per compute unit let the dispatcher balance
+  // the load, as long as a full-length split still has ~1024 rows to
+  // amortise its fixed costs (query load, merge, record store).
+  const long long bal = (16LL * cu_count + units - 1) / units;
+  const long long bal_cap = max_ctx / 1024;
+  const long long s_bal = bal < bal_cap ? bal : bal_cap;
+  if (s_bal > s) s = s_bal;
   // ... while a full-length split keeps at least 16 rows per query head of
   // the group, so the per-split fixed costs stay amortised.
   const long long min_rows = 16LL * group > 64 ? 16LL * group : 64;

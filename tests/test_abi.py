@@ -63,6 +63,17 @@ def test_pick_splits_properties(lib):
             assert blk * S >= T
         # never so many splits that a full-length split is tiny
         assert S == 1 or T // S >= 16
+    # Values the rule gives on 256 compute units. One sequence: one round of
+    # two resident workgroups per compute unit (4 KV heads -> 128), capped so
+    # a full-length split keeps 16 rows per grouped head (2048 / 112 -> 18).
+    # Batches: ~16 workgroups per compute unit, splits of >= 1024 rows.
+    cases = {(1, 28, 4, 128, 33024): 128, (1, 28, 4, 128, 2048): 18,
+             (1, 16, 2, 256, 8400): 65, (32, 32, 8, 128, 32768): 16,
+             (16, 32, 8, 128, 32768): 32, (8, 32, 8, 128, 32768): 32,
+             (4, 32, 8, 128, 32768): 32, (32, 32, 8, 128, 4096): 4,
+             (1, 4, 2, 64, 256): 4}
+    for shape, want in cases.items():
+        assert skv.pick_splits(*shape, cu_count=256) == (want, 0), shape
     with pytest.raises(skv.SplitKVError):
         skv.pick_splits(1, 28, 5, 128, 2048, 256)      # 28 % 5 != 0
     with pytest.raises(skv.SplitKVError):

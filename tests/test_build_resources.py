@@ -1,0 +1,56 @@
+"""Build check: no kernel uses scratch memory or spills registers.
+
+"10 · R4 — decode split-attention dim-parallel rewrite", sections 2.3 and 6:
+an accumulator sized at run time went to local memory and cost most of the
+old kernel's time; the accumulators here are sized at compile time and must
+stay in registers. The compiler's per-kernel resource report (written by
+decode_attention_gqa_amd/build.py) is checked for every instantiation.
+"""
+import os
+import re
+
+import pytest
+
+from decode_attention_gqa_amd import build
+
+
+def _report():
+    if not os.path.exists(build.RESOURCE_REPORT) or not os.path.exists(build.LIB):
+        build.build()
+    with open(build.RESOURCE_REPORT) as f:
+        return f.read()
+
+
+def _kernels(text):
+    """{mangled name: {field: value}} from the resource-usage remarks."""
+    out, cur = {}, None
+    for line in text.splitlines():
+        m = re.search(r"remark: Function Name: (\S+)", line)
+        if m:
+            cur = out.setdefault(m.group(1), {})
+            continue
+        m = re.search(r"remark:\s+([A-Za-z ]+?)(?: \[[^]]+\])?: (\d+)", line)
+        if m and cur is not None:
+            cur[m.group(1).strip()] = int(m.group(2))
+    return out
+
+
+def test_every_kernel_without_scratch_or_spills():
+    ks = _kernels(_report())
+    partial = [k for k in ks if "partial_" in k]
+    # 6 head dims x 8 group sizes, plus combine and probe kernels
+    assert len(partial) == 48, len(partial)
+    assert any("combine_kernel" in k for k in ks)
+    for name, f in ks.items():
+        assert f.get("ScratchSize", 0) == 0, (name, f)
+        assert f.get("VGPRs Spill", 0) == 0, (name, f)
+        assert f.get("SGPRs Spill", 0) == 0, (name, f)
+
+
+@pytest.mark.parametrize("hd,g,occ", [(128, 7, 2), (64, 8, 2), (256, 8, 1)])
+def test_matrix_core_kernel_occupancy(hd, g, occ):
+    ks = _kernels(_report())
+    name = [k for k in ks if f"partial_mfma_kernelILi{hd}ELi{g}E" in k]
+    assert name, (hd, g)
+    f = ks[name[0]]
+    assert f.get("Occupancy", 0) >= occ, f
