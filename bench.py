@@ -22,6 +22,9 @@ Reported (one JSON line on stdout):
 Usage: python bench.py [--steps K] [--warmup W] [--nkv N] [--layers L]
        python bench.py --sweep          # split-count sweep, one line per point
        python bench.py --mode kernels   # eager partial/combine launches + a copy
+       python bench.py --mode configs   # tiny / 7B@2K / hd256 workloads, warm+cold
+       python bench.py --mode ragged    # 32-sequence ragged batch, split sweep
+       python bench.py --mode oracle    # the fp64 oracle per workload (CPU only)
        python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --kernels-json F
                                         # fold two rocprofv3 --pmc runs
 """
@@ -66,20 +69,25 @@ def source_hash(paths=PARTIAL_SRCS) -> str:
 
 # --------------------------------------------------------------------------
 class Layers:
-    """L layers of the 28q/4kv hd128 cache, each in its own device buffers."""
+    """L layers of one decode shape, each layer's cache in its own buffers.
 
-    def __init__(self, layers: int, max_ctx: int, n_splits: int, block_len: int):
+    Default: the 28q/4kv hd128 growing-context cache with per-block score
+    offsets, max_ctx 33,024."""
+
+    def __init__(self, layers: int, max_ctx: int, n_splits: int, block_len: int,
+                 shape=None, case=None):
         import torch
 
         import decode_attention_gqa_amd as skv
         import synth
         self.torch, self.skv = torch, skv
-        sh = synth.Shape(1, 28, 4, 128, max_ctx)
+        sh = shape or synth.Shape(1, 28, 4, 128, max_ctx)
         self.shape = sh
         self.L = layers
         self.S, self.blk = n_splits, block_len
-        log(f"[bench] generating layer data: max_ctx={max_ctx}")
-        case = synth.make_offset_case(3, sh, max_ctx)
+        if case is None:
+            log(f"[bench] generating layer data: max_ctx={max_ctx}")
+            case = synth.make_offset_case(3, sh, max_ctx)
         self.case = case
         dev = torch.device("cuda", 0)
         k0 = torch.from_numpy(case.k).to(dev)
@@ -89,12 +97,13 @@ class Layers:
         self.k = [k0] + [k0.clone() for _ in range(layers - 1)]
         self.v = [v0] + [v0.clone() for _ in range(layers - 1)]
         self.q = [q0.clone() for _ in range(layers)]
-        self.pos = torch.zeros(1, dtype=torch.int32, device=dev)
-        nb = skv.partials_bytes(1, sh.n_head, sh.head_dim, n_splits)
+        self.pos = torch.from_numpy(case.positions.copy()).to(dev)
+        nb = skv.partials_bytes(sh.batch, sh.n_head, sh.head_dim, n_splits)
         self.part = [torch.empty(nb // 4, dtype=torch.float32, device=dev)
                      for _ in range(layers)]
-        self.out = [torch.empty((1, sh.n_head, sh.head_dim), dtype=torch.float32,
-                                device=dev) for _ in range(layers)]
+        self.out = [torch.empty((sh.batch, sh.n_head, sh.head_dim),
+                                dtype=torch.float32, device=dev)
+                    for _ in range(layers)]
         self.scale = case.scale
         torch.cuda.synchronize()
 
@@ -147,6 +156,34 @@ def time_replays(torch, graph, warmup: int, steps: int):
     per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
     total = evs[0].elapsed_time(evs[-1])
     return per, total, wall
+
+
+def time_replays_cold(torch, graph, flush, warmup: int, steps: int):
+    """Per-replay milliseconds with the Infinity Cache flushed before each
+    replay: a 1 GiB read of other data runs on the same stream just before
+    the first event, outside the timed window."""
+    for _ in range(warmup):
+        flush()
+        graph.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    a = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    b = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    for i in range(steps):
+        flush()
+        a[i].record(stream)
+        graph.replay()
+        b[i].record(stream)
+    torch.cuda.synchronize()
+    return [a[i].elapsed_time(b[i]) for i in range(steps)]
+
+
+def make_flush(torch, skv, gib: float = 1.0):
+    n = int(gib * (1 << 30))
+    buf = torch.zeros(n // 4, dtype=torch.int32, device="cuda")
+    grid = torch.cuda.get_device_properties(0).multi_processor_count * 16
+    sink = torch.zeros(grid, dtype=torch.int32, device="cuda")
+    return lambda: skv.probe_read(buf, sink, grid)
 
 
 def time_kernel(torch, launch, layers: int, reps: int):
@@ -417,6 +454,107 @@ def run_ragged(args):
         torch.cuda.empty_cache()
 
 
+def run_configs(args):
+    """The other decode workloads, one JSON line per (config, split) point:
+    7B shape at 2K (28 layers, 117 MB: fits the 256 MB Infinity Cache) and
+    the hd256 shape at 8,400 rows (12 layers, 206 MB) timed warm (cache-
+    resident after earlier replays) and cold (cache flushed before each
+    replay); the tiny case; the 32-sequence ragged batch at the heuristic."""
+    import torch
+
+    import decode_attention_gqa_amd as skv
+    import synth
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    flush = make_flush(torch, skv)
+
+    def emit(name, lay, S, blk, nkv_total):
+        graph = lay.capture()
+        kv = synth.kv_bytes(lay.shape.n_kv_head, lay.shape.head_dim,
+                            nkv_total) * lay.L
+        warm, _, _ = time_replays(torch, graph, args.warmup, args.steps)
+        cold = time_replays_cold(torch, graph, flush, args.warmup, args.steps)
+        del graph
+        p_us = time_kernel(torch, lay.partial, lay.L, args.kernel_reps)[0] * 1e3
+        c_us = time_kernel(torch, lay.combine, lay.L, args.kernel_reps)[0] * 1e3
+        h = skv.pick_splits(*dataclasses.astuple(lay.shape), cu) == (S, blk)
+        for label, per in (("warm", warm), ("cold", cold)):
+            med = statistics.median(per)
+            print(json.dumps({"config": name, "cache": label, "n_splits": S,
+                              "block_len": blk, "heuristic": h,
+                              "layers": lay.L,
+                              "us_per_layer": round(med * 1e3 / lay.L, 3),
+                              "kv_gbps": round(kv / (med * 1e-3) / 1e9, 1),
+                              "partial_avg_us": round(p_us, 3),
+                              "combine_avg_us": round(c_us, 3)}),
+                  flush=True)
+
+    sh = synth.CFG1
+    case = synth.make_case(1, sh, sh.max_ctx)
+    S, blk = skv.pick_splits(*dataclasses.astuple(sh), cu)
+    # 64 layers of separate buffers, so that one replay outlasts the host's
+    # submission of the next and the GPU time is what is measured
+    for S_, blk_ in sorted({(S, blk), (synth.CFG1_SPLITS, 0)}):
+        emit("tiny 4q/2kv hd64 nkv 256 x64 layers",
+             Layers(64, sh.max_ctx, S_, blk_, sh, case), S_, blk_, sh.max_ctx)
+
+    sh = synth.CFG2
+    case = synth.make_case(2, sh, sh.max_ctx)
+    S, blk = skv.pick_splits(*dataclasses.astuple(sh), cu)
+    for S_ in sorted(set(synth.CFG2_SPLIT_SWEEP) | {S} | set(args.extra_splits)):
+        lay = Layers(synth.CFG2_LAYERS, sh.max_ctx, S_, 0, sh, case)
+        emit("7B 28q/4kv hd128 nkv 2048 x28 layers", lay, S_, 0, sh.max_ctx)
+        del lay
+
+    sh = synth.CFG4
+    case = synth.make_case(4, sh, synth.CFG4_NKV)
+    pts = {skv.pick_splits(*dataclasses.astuple(sh), cu)}
+    pts |= {(-(-sh.max_ctx // b), b) for b in synth.CFG4_BLOCKS}
+    pts |= {(s_, 0) for s_ in args.extra_splits}
+    for S_, blk_ in sorted(pts):
+        lay = Layers(synth.CFG4_LAYERS, sh.max_ctx, S_, blk_, sh, case)
+        emit("hd256 16q/2kv nkv 8400 x12 layers", lay, S_, blk_, synth.CFG4_NKV)
+        del lay
+    torch.cuda.empty_cache()
+
+
+def run_oracle(args):
+    """The fp64 oracle (one thread) on each workload, median of 3 runs (one
+    run for the 32-sequence batch), one JSON line per point. Needs no GPU."""
+    import oracle
+    import synth
+
+    def timed(name, case, layers_note, reps=3):
+        sh = case.shape
+        runs = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            oracle.decode_attn(case.q, case.k, case.v, case.positions,
+                               sh.n_kv_head, case.scale)
+            runs.append(time.perf_counter() - t0)
+        med = statistics.median(runs)
+        kv = synth.kv_bytes(sh.n_kv_head, sh.head_dim, case.nkv)
+        print(json.dumps({"config": name, "kind": "oracle", "cores": 1,
+                          "ms_per_layer": round(med * 1e3, 2),
+                          "kv_gbps": round(kv / med / 1e9, 4),
+                          "note": layers_note}), flush=True)
+
+    sh = synth.CFG1
+    timed("tiny 4q/2kv hd64 nkv 256", synth.make_case(1, sh, sh.max_ctx), "1 layer")
+    sh = synth.CFG2
+    timed("7B 28q/4kv hd128 nkv 2048", synth.make_case(2, sh, sh.max_ctx),
+          "1 layer (of 28)")
+    sh = synth.CFG3
+    for nkv in (2048, 16384, 32768):
+        timed(f"7B 28q/4kv hd128 nkv {nkv}",
+              synth.make_offset_case(3, sh, nkv), "1 layer (of 28)")
+    sh = synth.CFG4
+    timed("hd256 16q/2kv nkv 8400", synth.make_case(4, sh, synth.CFG4_NKV),
+          "1 layer (of 12)")
+    sh = synth.CFG5
+    timed("ragged 32 x 32q/8kv hd128", synth.make_case(5, sh, synth.cfg5_lengths()),
+          "1 layer step, all 32 sequences; one run (~50 s)", reps=1)
+
+
 def run_sweep(args):
     import torch
 
@@ -515,9 +653,12 @@ def main():
                     metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--kernels-json", default=None)
     ap.add_argument("--write-traffic", default=None)
-    ap.add_argument("--mode", choices=["main", "kernels", "ragged"],
+    ap.add_argument("--mode", choices=["main", "kernels", "ragged", "configs",
+                                       "oracle"],
                     default="main")
     ap.add_argument("--ragged-batch", type=int, default=32)
+    ap.add_argument("--extra-splits", type=int, nargs="*", default=[],
+                    help="--mode configs: more split counts to time")
     ap.add_argument("--ragged-full", action="store_true",
                     help="every sequence at full length (uniform batch)")
     ap.add_argument("--copy-mib", type=int, default=256)
@@ -537,6 +678,10 @@ def main():
         run_kernels(args)
     elif args.mode == "ragged":
         run_ragged(args)
+    elif args.mode == "configs":
+        run_configs(args)
+    elif args.mode == "oracle":
+        run_oracle(args)
     else:
         run_main(args)
     return 0

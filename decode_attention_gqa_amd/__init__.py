@@ -40,6 +40,7 @@ SIGNATURES = {
     "splitkv_abi_version": (_i, []),
     "splitkv_strerror": (ctypes.c_char_p, [_i]),
     "splitkv_partials_bytes": (_sz, [_i, _i, _i, _i]),
+    "splitkv_workgroups_per_cu": (_i, [_i, _i]),
     "splitkv_pick_splits": (_i, [_i, _i, _i, _i, _i, _i,
                                  ctypes.POINTER(_i), ctypes.POINTER(_i)]),
     "splitkv_partial": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
@@ -99,6 +100,11 @@ def _check(status: int, what: str) -> None:
 
 def partials_bytes(batch: int, n_head: int, head_dim: int, n_splits: int) -> int:
     return int(load().splitkv_partials_bytes(batch, n_head, head_dim, n_splits))
+
+
+def workgroups_per_cu(head_dim: int, group: int) -> int:
+    """Resident partial-kernel workgroups per compute unit (0: unsupported)."""
+    return load().splitkv_workgroups_per_cu(head_dim, group)
 
 
 def pick_splits(batch: int, n_head: int, n_kv_head: int, head_dim: int,

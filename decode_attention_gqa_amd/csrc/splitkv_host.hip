@@ -137,6 +137,24 @@ size_t splitkv_partials_bytes(int batch, int n_head, int head_dim,
          (size_t)(4 + head_dim) * sizeof(float);
 }
 
+int splitkv_workgroups_per_cu(int head_dim, int group) {
+  if (!splitkv::head_dim_supported(head_dim) || group < 1 ||
+      group > splitkv::kMaxGroup)
+    return 0;
+  // From the compiler's resource report of each instantiation (waves per
+  // SIMD with one wave of the workgroup on each SIMD); a build check keeps
+  // this table equal to the report.
+  switch (head_dim) {
+    case 8: { static const int t[8] = {4, 4, 3, 3, 2, 2, 2, 2}; return t[group - 1]; }
+    case 16: { static const int t[8] = {4, 3, 3, 2, 2, 2, 2, 1}; return t[group - 1]; }
+    case 32: { static const int t[8] = {4, 3, 3, 2, 2, 2, 2, 1}; return t[group - 1]; }
+    case 64: return group == 1 ? 3 : 4;
+    case 128: return 2;
+    case 256: return 1;
+    default: return 0;
+  }
+}
+
 int splitkv_pick_splits(int batch, int n_head, int n_kv_head, int head_dim,
                         int max_ctx, int cu_count, int *n_splits,
                         int *block_len) {
@@ -146,9 +164,11 @@ int splitkv_pick_splits(int batch, int n_head, int n_kv_head, int head_dim,
   if (st != SPLITKV_OK) return st;
   const int group = n_head / n_kv_head;
   const long long units = (long long)batch * n_kv_head;
-  // One full round of resident workgroups (two per compute unit). With one
-  // sequence every split has the same work, so a single round is best.
-  long long s = (2LL * cu_count + units - 1) / units;
+  const long long wpc = splitkv_workgroups_per_cu(head_dim, group);
+  // One full round of resident workgroups. With one sequence every split
+  // has the same work, so a single round is best; a few workgroups past it
+  // would cost a whole second round, hence the floor.
+  long long s = wpc * cu_count / units;
   // With several sequences the lengths can differ and the host does not see
   // them: about 16 workgroups per compute unit let the dispatcher balance
   // the load, as long as a full-length split still has ~1024 rows to
@@ -156,13 +176,11 @@ int splitkv_pick_splits(int batch, int n_head, int n_kv_head, int head_dim,
   const long long bal = (16LL * cu_count + units - 1) / units;
   const long long bal_cap = max_ctx / 1024;
   const long long s_bal = bal < bal_cap ? bal : bal_cap;
-  if (s_bal > s) s = s_bal;
-  // ... while a full-length split keeps at least 16 rows per query head of
-  // the group, so the per-split fixed costs stay amortised.
-  const long long min_rows = 16LL * group > 64 ? 16LL * group : 64;
-  const long long cap = max_ctx / min_rows > 1 ? max_ctx / min_rows : 1;
-  if (s > cap) s = cap;
+  if (batch > 1 && s_bal > s) s = s_bal;
   if (s < 1) s = 1;
+  // A full-length split keeps at least two 16-row tiles.
+  const long long cap = max_ctx / 32 > 1 ? max_ctx / 32 : 1;
+  if (s > cap) s = cap;
   if (s > kMaxSplits) s = kMaxSplits;
   *n_splits = (int)s;
   *block_len = 0;

@@ -91,13 +91,30 @@ const char *splitkv_strerror(int status);
 size_t splitkv_partials_bytes(int batch, int n_head, int head_dim,
                               int n_splits);
 
+/* Partial-kernel workgroups that can be resident on one compute unit at
+ * once for (head_dim, group = n_head / n_kv_head), as the compiler's
+ * register and LDS allocation of that kernel instantiation allows (a
+ * workgroup is 4 waves, one per SIMD). Used by the split heuristic to size
+ * one full round of workgroups. Returns 0 for an unsupported pair. */
+int splitkv_workgroups_per_cu(int head_dim, int group);
+
 /* Split heuristic: chooses n_splits (and block_len, 0 = ceil rule) for a
  * shape, from the sequence capacity max_ctx and the GPU's compute-unit count.
  * The aim, from the pages: enough workgroups to fill the GPU ("10 · R4",
  * sections 1 and 3.1; dotLLM issue #199, comment 2, recommendation 1) while
  * each split keeps enough rows that its fixed costs (query load, record
  * write, merge) stay small ("10 · R4", section 3.3; "Red Lite dev35", the
- * block-length table). Host only; returns SPLITKV_OK or a negative status. */
+ * block-length table). The rule:
+ *   fill = floor(wpc * cu_count / (batch * n_kv_head)), wpc from
+ *          splitkv_workgroups_per_cu: one full round of resident workgroups,
+ *          never a partial second round;
+ *   bal  = min(ceil(16 * cu_count / (batch * n_kv_head)), max_ctx / 1024)
+ *          when batch > 1, else 0: with several sequences (lengths unknown
+ *          to the host) about 16 workgroups per compute unit balance uneven
+ *          lengths;
+ *   n_splits = min(max(fill, bal, 1), max(max_ctx / 32, 1), 65535): a
+ *          full-length split keeps at least two 16-row tiles.
+ * Host only; returns SPLITKV_OK or a negative status. */
 int splitkv_pick_splits(int batch, int n_head, int n_kv_head, int head_dim,
                         int max_ctx, int cu_count, int *n_splits,
                         int *block_len);

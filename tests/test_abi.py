@@ -61,19 +61,27 @@ def test_pick_splits_properties(lib):
         assert 1 <= S <= 65535 and blk >= 0
         if blk:
             assert blk * S >= T
-        # never so many splits that a full-length split is tiny
-        assert S == 1 or T // S >= 16
-    # Values the rule gives on 256 compute units. One sequence: one round of
-    # two resident workgroups per compute unit (4 KV heads -> 128), capped so
-    # a full-length split keeps 16 rows per grouped head (2048 / 112 -> 18).
-    # Batches: ~16 workgroups per compute unit, splits of >= 1024 rows.
-    cases = {(1, 28, 4, 128, 33024): 128, (1, 28, 4, 128, 2048): 18,
-             (1, 16, 2, 256, 8400): 65, (32, 32, 8, 128, 32768): 16,
+        # never so many splits that a full-length split is under two tiles
+        assert S == 1 or T // S >= 32
+    # Values the rule gives on 256 compute units. One sequence: one full round
+    # of resident workgroups (2 per compute unit at hd128 -> 128 splits over 4
+    # KV heads; 1 at hd256 -> 128 over 2), capped so a full-length split
+    # keeps two 16-row tiles (2048 / 32 -> 64; 256 / 32 -> 8). Batches: ~16
+    # workgroups per compute unit, splits of >= 1024 rows.
+    cases = {(1, 28, 4, 128, 33024): 128, (1, 28, 4, 128, 2048): 64,
+             (1, 16, 2, 256, 8400): 128, (32, 32, 8, 128, 32768): 16,
              (16, 32, 8, 128, 32768): 32, (8, 32, 8, 128, 32768): 32,
              (4, 32, 8, 128, 32768): 32, (32, 32, 8, 128, 4096): 4,
-             (1, 4, 2, 64, 256): 4}
+             (1, 4, 2, 64, 256): 8, (1, 28, 4, 128, 40): 1,
+             (1, 24, 3, 128, 33024): 170}
     for shape, want in cases.items():
         assert skv.pick_splits(*shape, cu_count=256) == (want, 0), shape
+    # never more than one round of resident workgroups for one sequence
+    for hd in (8, 16, 32, 64, 128, 256):
+        for g in range(1, 9):
+            for nkvh in (1, 2, 3, 4, 5, 8):
+                S, _ = skv.pick_splits(1, g * nkvh, nkvh, hd, 1 << 16, 256)
+                assert S * nkvh <= skv.workgroups_per_cu(hd, g) * 256, (hd, g)
     with pytest.raises(skv.SplitKVError):
         skv.pick_splits(1, 28, 5, 128, 2048, 256)      # 28 % 5 != 0
     with pytest.raises(skv.SplitKVError):

@@ -54,3 +54,22 @@ def test_matrix_core_kernel_occupancy(hd, g, occ):
     assert name, (hd, g)
     f = ks[name[0]]
     assert f.get("Occupancy", 0) >= occ, f
+
+
+def test_workgroups_per_cu_matches_compiler_report(splitkv_lib_path):
+    """The split heuristic sizes one round of workgroups from the library's
+    occupancy table; it must equal what the compiler reports for each
+    (head_dim, group) instantiation."""
+    import decode_attention_gqa_amd as skv
+    ks = _kernels(_report())
+    seen = 0
+    for name, f in ks.items():
+        m = re.search(r"partial_(?:mfma|valu)_kernelILi(\d+)ELi(\d+)E", name)
+        if not m:
+            continue
+        hd, g = int(m.group(1)), int(m.group(2))
+        assert skv.workgroups_per_cu(hd, g) == f["Occupancy"], (hd, g, f)
+        seen += 1
+    assert seen == 48
+    assert skv.workgroups_per_cu(96, 4) == 0
+    assert skv.workgroups_per_cu(128, 9) == 0
