@@ -13,6 +13,9 @@ cites the page passage it follows:
   ``positions[0] + 1``, split rule, idle splits) and 3.2 (record layout).
 * "Red Lite dev35 — long-context decode: grouped split-K attention", section
   Change (one workgroup per block and KV head, fixed block length).
+* dotLLM issue #199 (tensor-core decode attention), comment 1: section 1 (the
+  new K/V rows are written into the FP16 cache before attention) and section 2
+  (several query rows with a causal mask from positionOffset).
 """
 from __future__ import annotations
 
@@ -73,6 +76,20 @@ def load(path: str | None = None):
         lib.oracle_combine.argtypes = [_f64p, _f64p, ctypes.c_int, ctypes.c_int,
                                        ctypes.c_int, ctypes.c_int]
         lib.oracle_combine.restype = None
+        lib.oracle_f32_to_f16.argtypes = [ctypes.c_float]
+        lib.oracle_f32_to_f16.restype = ctypes.c_uint16
+        lib.oracle_f32_to_f16_array.argtypes = [_f32p, _u16p, ctypes.c_size_t]
+        lib.oracle_f32_to_f16_array.restype = None
+        lib.oracle_append_kv.argtypes = [_f32p, _f32p, _u16p, _u16p, _i32p,
+                                         ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int, ctypes.c_int,
+                                         ctypes.c_int]
+        lib.oracle_append_kv.restype = None
+        lib.oracle_decode_attn_rows.argtypes = [
+            _f32p, _u16p, _u16p, _i32p, _f64p, ctypes.c_int, ctypes.c_int,
+            ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+            ctypes.c_float, _f64p]
+        lib.oracle_decode_attn_rows.restype = None
         if path is None:
             _lib = lib
         return lib
@@ -160,4 +177,53 @@ def combine(records, lib=None) -> np.ndarray:
     hd = pstr - 4
     out = np.zeros((B, nh, hd), np.float64)
     lib.oracle_combine(rec, out, B, S, nh, hd)
+    return out
+
+
+def f32_to_f16(x, lib=None) -> np.ndarray:
+    """binary32 -> binary16 bits, round to nearest even (the oracle's own
+    conversion; #199 section 1 stores the cache in FP16)."""
+    lib = lib or load()
+    a = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.zeros(a.shape, np.uint16)
+    lib.oracle_f32_to_f16_array(a.ravel(), out.ravel(), a.size)
+    return out
+
+
+def append_kv(k_new, v_new, k_cache, v_cache, positions, lib=None):
+    """Caches after appending the new rows (#199 section 1): returns new
+    (k_cache, v_cache) uint16 arrays; the inputs are not modified.
+
+    k_new, v_new: fp32 [B][n_rows][n_kv_head][hd]; caches [B][max_ctx][nkvh][hd];
+    the last new row of sequence b lands at positions[b]."""
+    lib = lib or load()
+    kn = np.ascontiguousarray(k_new, dtype=np.float32)
+    vn = np.ascontiguousarray(v_new, dtype=np.float32)
+    B, n_rows, nkvh, hd = kn.shape
+    assert vn.shape == kn.shape
+    k = _u16(k_cache).copy()
+    v = _u16(v_cache).copy()
+    kb, max_ctx, knh, khd = k.shape
+    assert (kb, knh, khd) == (B, nkvh, hd) and v.shape == k.shape
+    pos = np.ascontiguousarray(positions, dtype=np.int32).reshape(B)
+    lib.oracle_append_kv(kn, vn, k, v, pos, B, n_rows, nkvh, hd, max_ctx)
+    return k, v
+
+
+def decode_attn_rows(q, k_cache, v_cache, positions, n_kv_head: int,
+                     scale: float, lib=None) -> np.ndarray:
+    """Several query rows per sequence with the causal mask of #199 section 2:
+    q fp32 [B][n_q][n_head][hd] -> out[B][n_q][n_head][hd] in double; row t
+    of sequence b sits at positions[b] - (n_q - 1 - t)."""
+    lib = lib or load()
+    q = np.ascontiguousarray(q, dtype=np.float32)
+    B, n_q, nh, hd = q.shape
+    kb, max_ctx, nkvh, khd = k_cache.shape
+    assert kb == B and nkvh == n_kv_head and khd == hd and nh % nkvh == 0
+    pos = np.ascontiguousarray(positions, dtype=np.int32).reshape(B)
+    out = np.zeros((B, n_q, nh, hd), np.float64)
+    work = np.zeros(max(max_ctx, 1), np.float64)
+    lib.oracle_decode_attn_rows(q, _u16(k_cache), _u16(v_cache), pos, out, B,
+                                n_q, nh, n_kv_head, hd, max_ctx,
+                                float(np.float32(scale)), work)
     return out

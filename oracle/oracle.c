@@ -255,3 +255,108 @@ void oracle_combine(const double *records, double *out, int batch,
         }
     }
 }
+
+/* ------------------------------------------------------------------------ */
+/* IEEE 754 binary32 -> binary16 with round-to-nearest, ties to even, from the
+ * formats' definitions. [#199] section 1: each decode step writes the new K/V
+ * row(s) into the FP16 cache before attention reads it; the conversion is
+ * the standard one (the page names no other rounding).
+ *   - NaN stays NaN (returned as the quiet NaN 0x7E00 with the input's sign;
+ *     the payload is not part of the definition);
+ *   - the magnitude is rounded to a multiple of the binary16 quantum at its
+ *     exponent: 2^(e-10) for a normal result with 2^e <= |x| < 2^(e+1),
+ *     e >= -14, and 2^-24 below 2^-14 (the subnormal range);
+ *   - a rounded magnitude of 2^16 or more is infinity (65504 is the largest
+ *     finite value; 65520, half a quantum above it, rounds to even, i.e. up).
+ * Every step is exact in double: x has 24 significant bits and the quanta are
+ * powers of two, so |x| / quantum is exact and rint() does the one rounding
+ * (in the default round-to-nearest-even mode). */
+uint16_t oracle_f32_to_f16(float x)
+{
+    const double v = (double)x;
+    const uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    if (isnan(v)) return (uint16_t)(sign | 0x7E00u);
+    const double a = fabs(v);
+    if (isinf(a)) return (uint16_t)(sign | 0x7C00u);
+    int e2;
+    frexp(a, &e2);             /* a = m * 2^e2, 0.5 <= m < 1, so 2^(e2-1) <= a */
+    int e = e2 - 1;
+    if (a == 0.0 || e < -14) e = -14;  /* subnormal range: quantum 2^-24 */
+    const double quantum = ldexp(1.0, e - 10);
+    const double r = rint(a / quantum) * quantum;   /* the one rounding */
+    if (r >= 65536.0) return (uint16_t)(sign | 0x7C00u);
+    if (r < ldexp(1.0, -14))                        /* subnormal or zero */
+        return (uint16_t)(sign | (uint16_t)(r / ldexp(1.0, -24)));
+    int re2;
+    frexp(r, &re2);            /* rounding may have carried into 2^(e+1) */
+    const int E = re2 - 1;
+    const unsigned frac = (unsigned)(r / ldexp(1.0, E - 10)) - 1024u;
+    return (uint16_t)(sign | (unsigned)((E + 15) << 10) | frac);
+}
+
+void oracle_f32_to_f16_array(const float *x, uint16_t *out, size_t n)
+{
+    for (size_t i = 0; i < n; ++i) out[i] = oracle_f32_to_f16(x[i]);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Cache append, [#199] section 1 (the step before attention): the n_rows new
+ * K and V rows of sequence b, fp32 [batch][n_rows][n_kv_head][head_dim], are
+ * converted to FP16 and stored at cache positions
+ *   p_t = positions[b] - (n_rows - 1) + t,   t = 0 .. n_rows-1,
+ * so that the last new row sits at positions[b] and the live length after the
+ * append is positions[b] + 1 (the same positions[] array then drives
+ * attention). Reading: rows whose p_t falls outside [0, max_ctx) are not
+ * written (the pages never write past the cache). Nothing else changes. */
+void oracle_append_kv(const float *k_new, const float *v_new,
+                      uint16_t *k_cache, uint16_t *v_cache,
+                      const int32_t *positions, int batch, int n_rows,
+                      int n_kv_head, int head_dim, int max_ctx)
+{
+    const size_t row = (size_t)n_kv_head * (size_t)head_dim;
+    for (int b = 0; b < batch; ++b) {
+        for (int t = 0; t < n_rows; ++t) {
+            const long long p = (long long)positions[b] - (n_rows - 1) + t;
+            if (p < 0 || p >= max_ctx) continue;
+            const size_t src = ((size_t)b * n_rows + t) * row;
+            const size_t dst = ((size_t)b * max_ctx + (size_t)p) * row;
+            for (size_t i = 0; i < row; ++i) {
+                k_cache[dst + i] = oracle_f32_to_f16(k_new[src + i]);
+                v_cache[dst + i] = oracle_f32_to_f16(v_new[src + i]);
+            }
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Several query rows per sequence, [#199] section 2: with seqQ > 1 new rows
+ * (speculative verification, chunked prefill) the mask inside the online
+ * softmax becomes causal, with the first new row at positionOffset. Reading:
+ * the n_q rows of sequence b sit at positions
+ *   positions[b] - (n_q - 1) + t,   t = 0 .. n_q-1
+ * (the last row at positions[b], so positionOffset = positions[b] - n_q + 1),
+ * and row t attends to cache rows j <= its own position: it is exactly a
+ * one-row decode with live length clamp(positions[b] - (n_q - 1 - t) + 1,
+ * 0, max_ctx). q and out: [batch][n_q][n_head][head_dim]. */
+void oracle_decode_attn_rows(const float *q, const uint16_t *k_cache,
+                             const uint16_t *v_cache, const int32_t *positions,
+                             double *out, int batch, int n_q, int n_head,
+                             int n_kv_head, int head_dim, int max_ctx,
+                             float scale, double *work /* >= max_ctx */)
+{
+    const size_t cache_seq = (size_t)max_ctx * n_kv_head * head_dim;
+    const size_t qrows = (size_t)n_head * head_dim;
+    for (int b = 0; b < batch; ++b) {
+        for (int t = 0; t < n_q; ++t) {
+            long long p = (long long)positions[b] - (n_q - 1 - t);
+            if (p < -1) p = -1;             /* live length 0 */
+            if (p > max_ctx) p = max_ctx;   /* live length max_ctx */
+            const int32_t pos = (int32_t)p;
+            const size_t qi = ((size_t)b * n_q + t) * qrows;
+            oracle_decode_attn(q + qi, k_cache + (size_t)b * cache_seq,
+                               v_cache + (size_t)b * cache_seq, &pos, out + qi,
+                               1, n_head, n_kv_head, head_dim, max_ctx, scale,
+                               work);
+        }
+    }
+}

@@ -320,3 +320,141 @@ def pin_combine_worked(lib):
     one = idle.copy()
     one[0, 1, 0] = [5.0, 2.0, 0, 0, 3.0, -1.0]
     assert np.array_equal(oracle.combine(one, lib)[0, 0], [1.5, -0.5])
+
+
+# --------------------------------------------------------------------------
+# The cache append (#199 section 1) and several query rows (#199 section 2).
+def _f16_bits_equal(ours, ref, what):
+    """Bit equality of binary16 patterns; NaN patterns compare as NaN only."""
+    ours = np.asarray(ours, np.uint16)
+    ref = np.asarray(ref, np.uint16)
+    nan_o = ((ours & 0x7C00) == 0x7C00) & ((ours & 0x03FF) != 0)
+    nan_r = ((ref & 0x7C00) == 0x7C00) & ((ref & 0x03FF) != 0)
+    assert np.array_equal(nan_o, nan_r), f"{what}: NaN positions differ"
+    bad = np.flatnonzero((ours != ref) & ~nan_r)
+    assert bad.size == 0, (f"{what}: {bad.size} patterns differ, first "
+                           f"ours {ours.flat[bad[0]]:#06x} ref {ref.flat[bad[0]]:#06x}")
+
+
+def pin_f32_to_f16_numpy(lib):
+    """binary32 -> binary16 equals numpy's conversion (an independent IEEE
+    round-to-nearest-even implementation) on special values, values spread
+    evenly over every exponent, and random bit patterns."""
+    rng = np.random.default_rng(160)
+    special = np.array([0.0, -0.0, np.inf, -np.inf, np.nan, 65504.0, 65519.996,
+                        65520.0, 65536.0, 1e9, 2.0**-24, 2.0**-25, 3 * 2.0**-26,
+                        2.0**-14, 2.0**-14 - 2.0**-25, 1e-30, -1e-30, 1.0,
+                        1.0 + 2.0**-11, 1.0 + 3 * 2.0**-11, 2049.0, 2051.0],
+                       np.float32)
+    spread = (rng.choice([-1.0, 1.0], 200_000) *
+              np.exp2(rng.uniform(-30, 17, 200_000))).astype(np.float32)
+    bits = rng.integers(0, 2**32, 200_000, dtype=np.uint64).astype(np.uint32)
+    for name, x in (("special", special), ("spread", spread),
+                    ("random bits", bits.view(np.float32))):
+        with np.errstate(over="ignore", invalid="ignore"):
+            ref = x.astype(np.float16).view(np.uint16)
+        _f16_bits_equal(oracle.f32_to_f16(x, lib=lib), ref, name)
+
+
+def pin_f32_to_f16_ties_and_round_trip(lib):
+    """Every finite binary16 value converts back to itself; the midpoint of
+    every pair of neighbours goes to the one with an even last bit (65520,
+    between 65504 and the first value past the range, goes to infinity); one
+    float32 step either side of a midpoint goes to the nearer neighbour."""
+    h = np.arange(0, 0x7C00, dtype=np.uint16)          # +0 .. 65504
+    vals = h.view(np.float16).astype(np.float32)
+    for sign in (0, 0x8000):
+        s = -1.0 if sign else 1.0
+        _f16_bits_equal(oracle.f32_to_f16(s * vals, lib=lib), h | sign,
+                        "round trip")
+        a = h.view(np.float16).astype(np.float64)
+        b = np.append(a[1:], 65536.0)                     # next value up
+        mid = ((a + b) / 2).astype(np.float32)            # exact in float32
+        assert np.array_equal(mid.astype(np.float64), (a + b) / 2)
+        nxt = np.append(h[1:], np.uint16(0x7C00))
+        even = np.where(h % 2 == 0, h, nxt).astype(np.uint16)
+        _f16_bits_equal(oracle.f32_to_f16(s * mid, lib=lib), even | sign, "ties")
+        up = np.nextafter(mid, np.float32(np.inf))
+        dn = np.nextafter(mid, np.float32(0))
+        _f16_bits_equal(oracle.f32_to_f16(s * up, lib=lib), nxt | sign, "above")
+        _f16_bits_equal(oracle.f32_to_f16(s * dn, lib=lib), h | sign, "below")
+
+
+def pin_append_kv(lib):
+    """Appending writes the fp16 of each new row at positions[b] - (n-1) + t
+    and nothing else; rows outside [0, max_ctx) are dropped. The expected
+    caches are built with numpy indexing and numpy's conversion."""
+    rng = np.random.default_rng(161)
+    B, nkvh, hd, T = 4, 2, 4, 8
+    for n_rows in (1, 3):
+        kc = rng.standard_normal((B, T, nkvh, hd)).astype(np.float16)
+        vc = rng.standard_normal((B, T, nkvh, hd)).astype(np.float16)
+        kn = (rng.standard_normal((B, n_rows, nkvh, hd)) * 300).astype(np.float32)
+        vn = rng.standard_normal((B, n_rows, nkvh, hd)).astype(np.float32)
+        kn[0, 0, 0, :4] = [np.nan, np.inf, 1e-7, 7e4]
+        pos = np.array([n_rows - 1, T - 1, T + 1, 1], np.int32)
+        ek = kc.view(np.uint16).copy()
+        ev = vc.view(np.uint16).copy()
+        for b in range(B):
+            for t in range(n_rows):
+                p = int(pos[b]) - (n_rows - 1) + t
+                if 0 <= p < T:
+                    with np.errstate(over="ignore", invalid="ignore"):
+                        ek[b, p] = kn[b, t].astype(np.float16).view(np.uint16)
+                        ev[b, p] = vn[b, t].astype(np.float16).view(np.uint16)
+        k2, v2 = oracle.append_kv(kn, vn, kc, vc, pos, lib=lib)
+        _f16_bits_equal(k2, ek, f"append K, {n_rows} rows")
+        _f16_bits_equal(v2, ev, f"append V, {n_rows} rows")
+
+
+def _causal_reference(q, k, v, pos, scale):
+    """Textbook masked attention in matrix form (numpy, double): for sequence
+    b, head h, S = Q Kᵀ scale over the whole cache, entries j > (row
+    position) set to -inf, row softmax, times V; a row with no keys is 0."""
+    B, n_q, nh, hd = q.shape
+    T, nkvh = k.shape[1], k.shape[2]
+    G = nh // nkvh
+    out = np.zeros((B, n_q, nh, hd))
+    for b in range(B):
+        rowpos = int(pos[b]) - (n_q - 1) + np.arange(n_q)
+        mask = np.arange(T)[None, :] > rowpos[:, None]
+        for h in range(nh):
+            Kf = k[b, :, h // G, :].astype(np.float64)
+            Vf = v[b, :, h // G, :].astype(np.float64)
+            S = q[b, :, h, :].astype(np.float64) @ Kf.T * float(np.float32(scale))
+            S[mask] = -np.inf
+            for t in range(n_q):
+                if not np.isfinite(S[t]).any():
+                    continue
+                w = np.exp(S[t] - S[t].max())
+                out[b, t, h] = (w @ Vf) / w.sum()
+    return out
+
+
+def pin_rows_causal(lib):
+    """Several query rows equal textbook causal attention: a prefill from
+    empty (rows at 0..n-1), a chunk after a cached prefix, a chunk whose
+    first rows sit before position 0 (no keys: output 0), and one single-row
+    decode."""
+    rng = np.random.default_rng(162)
+    B, nh, nkvh, hd, T = 4, 4, 2, 8, 12
+    for n_q in (1, 4):
+        q = rng.standard_normal((B, n_q, nh, hd)).astype(np.float32)
+        k = rng.standard_normal((B, T, nkvh, hd)).astype(np.float16)
+        v = rng.standard_normal((B, T, nkvh, hd)).astype(np.float16)
+        pos = np.array([n_q - 1, 9, 1, T - 1], np.int32)
+        scale = 0.35
+        got = oracle.decode_attn_rows(q, k, v, pos, nkvh, scale, lib=lib)
+        _close(got, _causal_reference(q, k, v, pos, scale), 1e-12,
+               f"causal rows n_q={n_q}")
+    # a chunk that fills the cache: every row sees exactly its prefix
+    q = rng.standard_normal((1, T, nh, hd)).astype(np.float32)
+    k = rng.standard_normal((1, T, nkvh, hd)).astype(np.float16)
+    v = rng.standard_normal((1, T, nkvh, hd)).astype(np.float16)
+    pos = np.array([T - 1], np.int32)
+    got = oracle.decode_attn_rows(q, k, v, pos, nkvh, 0.2, lib=lib)
+    _close(got, _causal_reference(q, k, v, pos, 0.2), 1e-12, "full prefill")
+    # row 0 of that prefill sees only key 0: exactly V[0]
+    G = nh // nkvh
+    for h in range(nh):
+        assert np.array_equal(got[0, 0, h], v[0, 0, h // G].astype(np.float64))

@@ -44,6 +44,24 @@ MUTANTS = {
         "const double w = exp(work[j]);\n                    const uint16_t"),
     "score_first_dim_only": ("for (int d = 0; d < head_dim; ++d)\n        dot +=",
                              "for (int d = 0; d < 1; ++d)\n        dot +="),
+    "f16_round_half_up": ("rint(a / quantum) * quantum", "floor(a / quantum + 0.5) * quantum"),
+    "f16_truncate": ("rint(a / quantum) * quantum", "floor(a / quantum) * quantum"),
+    "f16_subnormal_start": ("if (a == 0.0 || e < -14) e = -14;",
+                            "if (a == 0.0 || e < -15) e = -15;"),
+    "f16_nan_to_inf": ("if (isnan(v)) return (uint16_t)(sign | 0x7E00u);",
+                       "if (isnan(v)) return (uint16_t)(sign | 0x7C00u);"),
+    "append_row_offset": ("const long long p = (long long)positions[b] - (n_rows - 1) + t;",
+                          "const long long p = (long long)positions[b] + t - n_rows;"),
+    "append_drops_last_row": ("if (p < 0 || p >= max_ctx) continue;",
+                              "if (p < 0 || p >= max_ctx - 1) continue;"),
+    "append_k_from_v": ("k_cache[dst + i] = oracle_f32_to_f16(k_new[src + i]);",
+                        "k_cache[dst + i] = oracle_f32_to_f16(v_new[src + i]);"),
+    "rows_no_causal": ("long long p = (long long)positions[b] - (n_q - 1 - t);",
+                       "long long p = (long long)positions[b];"),
+    "rows_shift": ("long long p = (long long)positions[b] - (n_q - 1 - t);",
+                   "long long p = (long long)positions[b] - (n_q - t);"),
+    "rows_reversed": ("const size_t qi = ((size_t)b * n_q + t) * qrows;",
+                      "const size_t qi = ((size_t)b * n_q + (n_q - 1 - t)) * qrows;"),
 }
 
 PINS = [f for n, f in inspect.getmembers(oracle_pins, inspect.isfunction)
