@@ -25,6 +25,7 @@ Usage: python bench.py [--steps K] [--warmup W] [--nkv N] [--layers L]
        python bench.py --mode configs   # tiny / 7B@2K / hd256 workloads, warm+cold
        python bench.py --mode ragged    # 32-sequence ragged batch, split sweep
        python bench.py --mode oracle    # the fp64 oracle per workload (CPU only)
+       python bench.py --mode step      # append + partial + combine per layer
        python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --kernels-json F
                                         # fold two rocprofv3 --pmc runs
 """
@@ -370,8 +371,9 @@ def run_main(args):
 
 
 def run_kernels(args):
-    """Counter-collection workload: each layer's partial and combine launched
-    eagerly, then a plain copy of known size (the counter scale)."""
+    """Profiler workload: graphs of each layer's partial, combine and KV-cache
+    append launches (HIP-event timed), then a plain copy of known size (the
+    counter scale)."""
     import torch
 
     import decode_attention_gqa_amd as skv
@@ -386,6 +388,13 @@ def run_kernels(args):
     lay.set_nkv(args.nkv)
     p_mean, _ = time_kernel(torch, lay.partial, args.layers, args.kernel_reps)
     c_mean, _ = time_kernel(torch, lay.combine, args.layers, args.kernel_reps)
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(3)
+    kn = torch.randn((1, 1, 4, 128), generator=gen, device="cuda")
+    vn = torch.randn((1, 1, 4, 128), generator=gen, device="cuda")
+    a_mean, _ = time_kernel(
+        torch, lambda l: skv.append_kv(kn, vn, lay.k[l], lay.v[l], lay.pos),
+        args.layers, args.kernel_reps)
     nbytes = args.copy_mib << 20
     src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
     dst = torch.empty_like(src)
@@ -396,6 +405,7 @@ def run_kernels(args):
                       "partial_launches": 6 * args.kernel_reps + args.layers,
                       "partial_avg_us_events": round(p_mean * 1e3, 3),
                       "combine_avg_us_events": round(c_mean * 1e3, 3),
+                      "append_avg_us_events": round(a_mean * 1e3, 3),
                       "copy_bytes": nbytes,
                       "kv_bytes_per_partial": synth.kv_bytes(4, 128, args.nkv),
                       "partial_src_sha256_16": source_hash()}), flush=True)
@@ -555,6 +565,60 @@ def run_oracle(args):
           "1 layer step, all 32 sequences; one run (~50 s)", reps=1)
 
 
+def run_step(args):
+    """A whole decode step per layer: KV-cache append of the new row, then
+    partial + combine, 28 layers in one graph, at several live lengths; plus
+    the append kernel alone (graph of launches, HIP events)."""
+    import torch
+
+    import decode_attention_gqa_amd as skv
+    import synth
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    max_ctx = synth.CFG3.max_ctx
+    S, blk = skv.pick_splits(1, 28, 4, 128, max_ctx, cu)
+    lay = Layers(args.layers, max_ctx, S, blk)
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev)
+    g.manual_seed(3)
+    kn = [torch.randn((1, 1, 4, 128), generator=g, device=dev)
+          for _ in range(lay.L)]
+    vn = [torch.randn((1, 1, 4, 128), generator=g, device=dev)
+          for _ in range(lay.L)]
+
+    def append(l):
+        skv.append_kv(kn[l], vn[l], lay.k[l], lay.v[l], lay.pos)
+
+    def full():
+        for l in range(lay.L):
+            append(l)
+            skv.decode_attn(lay.q[l], lay.k[l], lay.v[l], lay.pos, lay.part[l],
+                            lay.out[l], S, blk, lay.scale)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        full()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        full()
+    torch.cuda.synchronize()
+    a_mean, _ = time_kernel(torch, append, lay.L, args.kernel_reps)
+    row_bytes = 4 * 128 * (4 + 4 + 2 + 2)   # K,V fp32 read + fp16 written
+    for nkv in args.points:
+        lay.set_nkv(nkv)
+        per, _, _ = time_replays(torch, graph, args.warmup, args.steps)
+        med = statistics.median(per)
+        kv = synth.kv_bytes(4, 128, nkv) * lay.L
+        print(json.dumps({"decode_step": True, "nkv": nkv, "n_splits": S,
+                          "layers": lay.L,
+                          "us_per_layer": round(med * 1e3 / lay.L, 3),
+                          "kv_gbps": round(kv / (med * 1e-3) / 1e9, 1),
+                          "append_avg_us": round(a_mean * 1e3, 3),
+                          "append_bytes": row_bytes}), flush=True)
+
+
 def run_sweep(args):
     import torch
 
@@ -654,7 +718,7 @@ def main():
     ap.add_argument("--kernels-json", default=None)
     ap.add_argument("--write-traffic", default=None)
     ap.add_argument("--mode", choices=["main", "kernels", "ragged", "configs",
-                                       "oracle"],
+                                       "oracle", "step"],
                     default="main")
     ap.add_argument("--ragged-batch", type=int, default=32)
     ap.add_argument("--extra-splits", type=int, nargs="*", default=[],
@@ -682,6 +746,8 @@ def main():
         run_configs(args)
     elif args.mode == "oracle":
         run_oracle(args)
+    elif args.mode == "step":
+        run_step(args)
     else:
         run_main(args)
     return 0

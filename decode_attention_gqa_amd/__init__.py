@@ -8,7 +8,8 @@ status into ``SplitKVError``. Every step of the computation runs in the HIP
 kernels. There is no fallback: if the library is missing, every call raises.
 
 Names follow the C ABI: ``decode_attn``, ``partial``, ``combine``,
-``partials_bytes``, ``pick_splits``, ``strerror``.
+``append_kv``, ``partials_bytes``, ``pick_splits``, ``workgroups_per_cu``,
+``strerror``.
 """
 from __future__ import annotations
 
@@ -18,7 +19,8 @@ import os
 import threading
 
 __all__ = ["SplitKVError", "load", "abi_version", "strerror", "partials_bytes",
-           "pick_splits", "partial", "combine", "decode_attn", "probe_read",
+           "pick_splits", "partial", "combine", "decode_attn", "append_kv",
+           "workgroups_per_cu", "probe_read",
            "probe_copy", "LIB_PATH", "SUPPORTED_HEAD_DIMS", "MAX_GROUP"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
@@ -48,6 +50,8 @@ SIGNATURES = {
     "splitkv_combine": (_i, [_vp, _vp, _i, _i, _i, _i, _vp]),
     "splitkv_decode_attn": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
                                  _i, _i, _i, _f, _vp]),
+    "splitkv_append_kv": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
+                               _vp]),
     "splitkv_probe_read": (_i, [_vp, _sz, _vp, _i, _vp]),
     "splitkv_probe_copy": (_i, [_vp, _vp, _sz, _i, _vp]),
 }
@@ -210,6 +214,33 @@ def decode_attn(q, k_cache, v_cache, positions, partials, out, n_splits: int,
         positions.data_ptr(), partials.data_ptr(), out.data_ptr(), B, nh, nkvh,
         hd, max_ctx, n_splits, block_len, scale, _stream_ptr(stream)),
         "splitkv_decode_attn")
+
+
+def append_kv(k_new, v_new, k_cache, v_cache, positions, stream=None):
+    """KV-cache append: new fp32 rows [B][n_rows][n_kv_head][hd] into the
+    fp16 caches [B][max_ctx][n_kv_head][hd]; the last new row of sequence b
+    lands at positions[b] (read on the device)."""
+    torch = _torch()
+    _need(k_new, (torch.float32,), "k_new")
+    _need(v_new, (torch.float32,), "v_new")
+    _need(k_cache, (torch.float16, torch.int16, torch.uint16), "k_cache")
+    _need(v_cache, (torch.float16, torch.int16, torch.uint16), "v_cache")
+    _need(positions, (torch.int32,), "positions")
+    if k_new.dim() != 4 or k_cache.dim() != 4:
+        raise ValueError("k_new must be [B][n_rows][n_kv_head][hd], "
+                         "k_cache [B][max_ctx][n_kv_head][hd]")
+    B, n_rows, nkvh, hd = k_new.shape
+    kb, max_ctx, knh, khd = k_cache.shape
+    if (tuple(v_new.shape) != tuple(k_new.shape) or
+            tuple(v_cache.shape) != tuple(k_cache.shape) or
+            (kb, knh, khd) != (B, nkvh, hd)):
+        raise ValueError("k_new, v_new, k_cache and v_cache shapes disagree")
+    if positions.numel() != B:
+        raise ValueError("positions must hold one entry per sequence")
+    _check(load().splitkv_append_kv(
+        k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), positions.data_ptr(), B, n_rows, nkvh, hd, max_ctx,
+        _stream_ptr(stream)), "splitkv_append_kv")
 
 
 def probe_read(buf, sink, grid: int, stream=None):

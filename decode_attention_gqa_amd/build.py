@@ -25,7 +25,7 @@ RESOURCE_REPORT = os.path.join(BUILD, "resource_usage.txt")
 
 SOURCES = ["splitkv_host.hip", "splitkv_partial.hip",
            "splitkv_partial_valu.hip", "splitkv_partial_mfma.hip",
-           "splitkv_combine.hip", "splitkv_probe.hip"]
+           "splitkv_combine.hip", "splitkv_append.hip", "splitkv_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",

@@ -227,6 +227,35 @@ int splitkv_decode_attn(const float *q, const uint16_t *k_cache,
   return do_combine(partials, out, batch, n_head, head_dim, n_splits, stream);
 }
 
+int splitkv_append_kv(const float *k_new, const float *v_new,
+                      uint16_t *k_cache, uint16_t *v_cache,
+                      const int32_t *positions, int batch, int n_rows,
+                      int n_kv_head, int head_dim, int max_ctx, void *stream) {
+  if (!k_new || !v_new || !k_cache || !v_cache || !positions)
+    return SPLITKV_EINVAL;
+  if (batch < 1 || n_rows < 1 || n_kv_head < 1 || max_ctx < 1)
+    return SPLITKV_EINVAL;
+  if (!splitkv::head_dim_supported(head_dim)) return SPLITKV_EUNSUPPORTED;
+  if (batch > kMaxGridYZ || n_rows > kMaxGridYZ || n_kv_head > kMaxGridYZ)
+    return SPLITKV_EINVAL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16) || !aligned(k_cache, 16) ||
+      !aligned(v_cache, 16) || !aligned(positions, 4))
+    return SPLITKV_EALIGN;
+  splitkv::AppendArgs a;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.positions = positions;
+  a.n_rows = n_rows;
+  a.row_elems = n_kv_head * head_dim;
+  a.max_ctx = max_ctx;
+  return splitkv::launch_append(a, batch, static_cast<hipStream_t>(stream)) ==
+                 hipSuccess
+             ? SPLITKV_OK
+             : SPLITKV_ELAUNCH;
+}
+
 int splitkv_probe_read(const void *buf, size_t bytes, uint32_t *sink,
                        int grid, void *stream) {
   if (!buf || !sink || bytes == 0 || bytes % 16 != 0 || grid < 1 ||

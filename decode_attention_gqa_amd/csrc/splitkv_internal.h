@@ -30,12 +30,25 @@ struct CombineArgs {
   int n_splits;
 };
 
+// Arguments of the KV-cache append kernel.
+struct AppendArgs {
+  const float *k_new;        // [B][n_rows][n_kv_head][head_dim] fp32
+  const float *v_new;        // same layout
+  uint16_t *k_cache;         // [B][max_ctx][n_kv_head][head_dim] fp16 bits
+  uint16_t *v_cache;         // same layout
+  const int32_t *positions;  // [B]; the last new row goes to positions[b]
+  int n_rows;
+  int row_elems;             // n_kv_head * head_dim (a multiple of 8)
+  int max_ctx;
+};
+
 // Launchers: enqueue one kernel on `stream` and return hipGetLastError().
 // The host code validates every argument before calling them.
 hipError_t launch_partial(int head_dim, int group, const PartialArgs &a,
                           int batch, hipStream_t stream);
 hipError_t launch_combine(int head_dim, const CombineArgs &a, int batch,
                           hipStream_t stream);
+hipError_t launch_append(const AppendArgs &a, int batch, hipStream_t stream);
 hipError_t launch_probe_read(const void *buf, size_t bytes, uint32_t *sink,
                              int grid, hipStream_t stream);
 hipError_t launch_probe_copy(const void *src, void *dst, size_t bytes,

@@ -139,6 +139,27 @@ int splitkv_decode_attn(const float *q, const uint16_t *k_cache,
                         int n_kv_head, int head_dim, int max_ctx, int n_splits,
                         int block_len, float scale, void *stream);
 
+/* KV-cache append, the step before attention in a decode step (dotLLM issue
+ * #199, comment 1, section 1: the new K/V rows are written into the FP16
+ * cache, then attention reads the cache).
+ *   k_new, v_new      device, fp32 [batch][n_rows][n_kv_head][head_dim],
+ *                     16-byte aligned; read only.
+ *   k_cache, v_cache  device, fp16 bits [batch][max_ctx][n_kv_head][head_dim],
+ *                     16-byte aligned; row t of sequence b is written at
+ *                     position positions[b] - (n_rows - 1) + t (the last new
+ *                     row at positions[b], so the live length afterwards is
+ *                     positions[b] + 1); rows whose position falls outside
+ *                     [0, max_ctx) are skipped; nothing else is written.
+ *   positions         device int32 [batch], read on the device (a captured
+ *                     graph appends at the current length on every replay).
+ * Conversion: fp32 -> fp16 round to nearest even, overflow to infinity, NaN
+ * stays NaN. k_new/v_new must not overlap the caches. Enqueued on `stream`;
+ * errors as for splitkv_partial. */
+int splitkv_append_kv(const float *k_new, const float *v_new,
+                      uint16_t *k_cache, uint16_t *v_cache,
+                      const int32_t *positions, int batch, int n_rows,
+                      int n_kv_head, int head_dim, int max_ctx, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -209,3 +209,33 @@ def test_probe_rejects(lib):
 def test_missing_library_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         skv.load(str(tmp_path / "nope.so"))
+
+
+BAD_APPEND = [
+    ("null k_new", dict(kn=0), EINVAL),
+    ("null v_new", dict(vn=0), EINVAL),
+    ("null k_cache", dict(kc=0), EINVAL),
+    ("null v_cache", dict(vc=0), EINVAL),
+    ("null positions", dict(pos=0), EINVAL),
+    ("batch 0", dict(B=0), EINVAL),
+    ("n_rows 0", dict(n=0), EINVAL),
+    ("n_rows too big", dict(n=65536), EINVAL),
+    ("n_kv_head 0", dict(nkvh=0), EINVAL),
+    ("max_ctx 0", dict(T=0), EINVAL),
+    ("head_dim 96", dict(hd=96), EUNSUP),
+    ("k_new misaligned", dict(kn=A + 4), EALIGN),
+    ("v_cache misaligned", dict(vc=A + 0x3000 + 8), EALIGN),
+    ("positions misaligned", dict(pos=A + 0x4000 + 2), EALIGN),
+]
+
+
+@cpu_only
+@pytest.mark.parametrize("what,over,code", BAD_APPEND,
+                         ids=[c[0] for c in BAD_APPEND])
+def test_append_rejects(lib, what, over, code):
+    a = dict(kn=A, vn=A + 0x1000, kc=A + 0x2000, vc=A + 0x3000, pos=A + 0x4000,
+             B=2, n=1, nkvh=4, hd=128, T=2048)
+    a.update(over)
+    assert lib.splitkv_append_kv(a["kn"], a["vn"], a["kc"], a["vc"], a["pos"],
+                                 a["B"], a["n"], a["nkvh"], a["hd"], a["T"],
+                                 None) == code
