@@ -26,6 +26,8 @@ Usage: python bench.py [--steps K] [--warmup W] [--nkv N] [--layers L]
        python bench.py --mode ragged    # 32-sequence ragged batch, split sweep
        python bench.py --mode oracle    # the fp64 oracle per workload (CPU only)
        python bench.py --mode step      # append + partial + combine per layer
+       python bench.py --mode per_head --sweep-splits 18 36 64 128
+                                        # grouped vs per-query-head grid
        python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --kernels-json F
                                         # fold two rocprofv3 --pmc runs
 """
@@ -386,6 +388,10 @@ def run_kernels(args):
         S, blk = skv.pick_splits(1, 28, 4, 128, max_ctx, cu)
     lay = Layers(args.layers, max_ctx, S, blk)
     lay.set_nkv(args.nkv)
+    if args.per_head:   # the per-query-head form in place of the grouped one
+        lay.partial = lambda l: skv.partial_per_head(
+            lay.q[l], lay.k[l], lay.v[l], lay.pos, lay.part[l], S, blk,
+            lay.scale)
     p_mean, _ = time_kernel(torch, lay.partial, args.layers, args.kernel_reps)
     c_mean, _ = time_kernel(torch, lay.combine, args.layers, args.kernel_reps)
     gen = torch.Generator(device="cuda")
@@ -400,7 +406,8 @@ def run_kernels(args):
     dst = torch.empty_like(src)
     skv.probe_copy(src, dst, cu * 16)
     torch.cuda.synchronize()
-    print(json.dumps({"mode": "kernels", "nkv": args.nkv, "n_splits": S,
+    print(json.dumps({"mode": "kernels", "per_head": args.per_head,
+                      "nkv": args.nkv, "n_splits": S,
                       "block_len": blk, "layers": args.layers,
                       "partial_launches": 6 * args.kernel_reps + args.layers,
                       "partial_avg_us_events": round(p_mean * 1e3, 3),
@@ -619,6 +626,59 @@ def run_step(args):
                           "append_bytes": row_bytes}), flush=True)
 
 
+def run_per_head(args):
+    """A/B of the partial kernel's grid: grouped (one workgroup per split and
+    KV head, all G query heads) against per-query-head (one workgroup per
+    split and query head, every KV row read G times). 28 layers of partial +
+    combine in one graph per variant and split count, plus the partial kernel
+    alone."""
+    import torch
+
+    import decode_attention_gqa_amd as skv
+    import synth
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    max_ctx = synth.CFG3.max_ctx
+    S_g, _ = skv.pick_splits(1, 28, 4, 128, max_ctx, cu)
+    variants = [("grouped", S_g)] + [("per_head", s) for s in args.sweep_splits]
+    for form, S in variants:
+        lay = Layers(args.layers, max_ctx, S, 0)
+        part_fn = skv.partial if form == "grouped" else skv.partial_per_head
+
+        def step():
+            for l in range(lay.L):
+                part_fn(lay.q[l], lay.k[l], lay.v[l], lay.pos, lay.part[l], S, 0,
+                        lay.scale)
+                skv.combine(lay.part[l], lay.out[l], S)
+
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        for nkv in args.points:
+            lay.set_nkv(nkv)
+            per, _, _ = time_replays(torch, graph, args.warmup, args.steps)
+            med = statistics.median(per)
+            p_us = time_kernel(
+                torch, lambda l: part_fn(lay.q[l], lay.k[l], lay.v[l], lay.pos,
+                                         lay.part[l], S, 0, lay.scale),
+                lay.L, args.kernel_reps)[0] * 1e3
+            kv = synth.kv_bytes(4, 128, nkv)
+            print(json.dumps({"form": form, "n_splits": S, "nkv": nkv,
+                              "workgroups": S * (4 if form == "grouped" else 28),
+                              "us_per_layer": round(med * 1e3 / lay.L, 3),
+                              "partial_avg_us": round(p_us, 3),
+                              "partial_kv_gbps": round(kv / (p_us * 1e-6) / 1e9,
+                                                       1)}), flush=True)
+        del graph, lay
+        torch.cuda.empty_cache()
+
+
 def run_sweep(args):
     import torch
 
@@ -718,9 +778,11 @@ def main():
     ap.add_argument("--kernels-json", default=None)
     ap.add_argument("--write-traffic", default=None)
     ap.add_argument("--mode", choices=["main", "kernels", "ragged", "configs",
-                                       "oracle", "step"],
+                                       "oracle", "step", "per_head"],
                     default="main")
     ap.add_argument("--ragged-batch", type=int, default=32)
+    ap.add_argument("--per-head", action="store_true",
+                    help="--mode kernels: time the per-query-head partial form")
     ap.add_argument("--extra-splits", type=int, nargs="*", default=[],
                     help="--mode configs: more split counts to time")
     ap.add_argument("--ragged-full", action="store_true",
@@ -748,6 +810,8 @@ def main():
         run_oracle(args)
     elif args.mode == "step":
         run_step(args)
+    elif args.mode == "per_head":
+        run_per_head(args)
     else:
         run_main(args)
     return 0

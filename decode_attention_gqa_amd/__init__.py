@@ -7,7 +7,8 @@ passes their device pointers and the current HIP stream, and turns a negative
 status into ``SplitKVError``. Every step of the computation runs in the HIP
 kernels. There is no fallback: if the library is missing, every call raises.
 
-Names follow the C ABI: ``decode_attn``, ``partial``, ``combine``,
+Names follow the C ABI: ``decode_attn``, ``partial``, ``partial_per_head``,
+``combine``,
 ``append_kv``, ``partials_bytes``, ``pick_splits``, ``workgroups_per_cu``,
 ``strerror``.
 """
@@ -19,7 +20,8 @@ import os
 import threading
 
 __all__ = ["SplitKVError", "load", "abi_version", "strerror", "partials_bytes",
-           "pick_splits", "partial", "combine", "decode_attn", "append_kv",
+           "pick_splits", "partial", "partial_per_head", "combine",
+           "decode_attn", "append_kv",
            "workgroups_per_cu", "probe_read",
            "probe_copy", "LIB_PATH", "SUPPORTED_HEAD_DIMS", "MAX_GROUP"]
 
@@ -47,6 +49,8 @@ SIGNATURES = {
                                  ctypes.POINTER(_i), ctypes.POINTER(_i)]),
     "splitkv_partial": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
                              _i, _f, _vp]),
+    "splitkv_partial_per_head": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
+                                      _i, _i, _i, _f, _vp]),
     "splitkv_combine": (_i, [_vp, _vp, _i, _i, _i, _i, _vp]),
     "splitkv_decode_attn": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
                                  _i, _i, _i, _f, _vp]),
@@ -184,6 +188,20 @@ def partial(q, k_cache, v_cache, positions, partials, n_splits: int,
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         positions.data_ptr(), partials.data_ptr(), B, nh, nkvh, hd, max_ctx,
         n_splits, block_len, scale, _stream_ptr(stream)), "splitkv_partial")
+
+
+def partial_per_head(q, k_cache, v_cache, positions, partials, n_splits: int,
+                     block_len: int = 0, scale: float | None = None,
+                     stream=None):
+    """Partial kernel, per-query-head grid (A/B baseline; same records)."""
+    B, nh, nkvh, hd, max_ctx = _shapes(q, k_cache, v_cache, positions)
+    _partials_ok(partials, B, nh, hd, n_splits)
+    scale = 1.0 / math.sqrt(hd) if scale is None else float(scale)
+    _check(load().splitkv_partial_per_head(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        positions.data_ptr(), partials.data_ptr(), B, nh, nkvh, hd, max_ctx,
+        n_splits, block_len, scale, _stream_ptr(stream)),
+        "splitkv_partial_per_head")
 
 
 def combine(partials, out, n_splits: int, stream=None):

@@ -82,7 +82,8 @@ int check_combine(const float *partials, const float *out, int batch,
 int do_partial(const float *q, const uint16_t *k, const uint16_t *v,
                const int32_t *positions, float *partials, int batch,
                int n_head, int n_kv_head, int head_dim, int max_ctx,
-               int n_splits, int block_len, float scale, void *stream) {
+               int n_splits, int block_len, float scale, void *stream,
+               bool per_head = false) {
   splitkv::PartialArgs a;
   a.q = q;
   a.k = k;
@@ -95,9 +96,12 @@ int do_partial(const float *q, const uint16_t *k, const uint16_t *v,
   a.n_splits = n_splits;
   a.block_len = block_len;
   a.scale_log2 = (float)((double)scale * kLog2e);
+  a.kv_group = n_head / n_kv_head;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e =
-      splitkv::launch_partial(head_dim, n_head / n_kv_head, a, batch,
-                              static_cast<hipStream_t>(stream));
+      per_head ? splitkv::launch_partial_per_head(head_dim, a, batch, s)
+               : splitkv::launch_partial(head_dim, n_head / n_kv_head, a,
+                                         batch, s);
   return e == hipSuccess ? SPLITKV_OK : SPLITKV_ELAUNCH;
 }
 
@@ -178,7 +182,7 @@ int splitkv_pick_splits(int batch, int n_head, int n_kv_head, int head_dim,
   const long long s_bal = bal < bal_cap ? bal : bal_cap;
   if (batch > 1 && s_bal > s) s = s_bal;
   if (s < 1) s = 1;
-  // A full-length split keeps at least two 16-row tiles.
+  // A full-length split keeps at least 32 rows (one wave's tile).
   const long long cap = max_ctx / 32 > 1 ? max_ctx / 32 : 1;
   if (s > cap) s = cap;
   if (s > kMaxSplits) s = kMaxSplits;
@@ -225,6 +229,23 @@ int splitkv_decode_attn(const float *q, const uint16_t *k_cache,
                   stream);
   if (st != SPLITKV_OK) return st;
   return do_combine(partials, out, batch, n_head, head_dim, n_splits, stream);
+}
+
+int splitkv_partial_per_head(const float *q, const uint16_t *k_cache,
+                             const uint16_t *v_cache, const int32_t *positions,
+                             float *partials, int batch, int n_head,
+                             int n_kv_head, int head_dim, int max_ctx,
+                             int n_splits, int block_len, float scale,
+                             void *stream) {
+  const int st = check_partial(q, k_cache, v_cache, positions, partials, batch,
+                               n_head, n_kv_head, head_dim, max_ctx, n_splits,
+                               block_len, scale);
+  if (st != SPLITKV_OK) return st;
+  if (head_dim < 64) return SPLITKV_EUNSUPPORTED;   // matrix-core family only
+  if (n_head > kMaxGridYZ) return SPLITKV_EINVAL;
+  return do_partial(q, k_cache, v_cache, positions, partials, batch, n_head,
+                    n_kv_head, head_dim, max_ctx, n_splits, block_len, scale,
+                    stream, true);
 }
 
 int splitkv_append_kv(const float *k_new, const float *v_new,

@@ -21,6 +21,7 @@ struct PartialArgs {
   int n_splits;
   int block_len;             // 0: chunk = ceil(nkv / n_splits)
   float scale_log2;          // scale * log2(e): scores are kept in base-2 units
+  int kv_group;              // per-query-head form only: n_head / n_kv_head
 };
 
 struct CombineArgs {
@@ -48,6 +49,8 @@ hipError_t launch_partial(int head_dim, int group, const PartialArgs &a,
                           int batch, hipStream_t stream);
 hipError_t launch_combine(int head_dim, const CombineArgs &a, int batch,
                           hipStream_t stream);
+hipError_t launch_partial_per_head(int head_dim, const PartialArgs &a,
+                                   int batch, hipStream_t stream);
 hipError_t launch_append(const AppendArgs &a, int batch, hipStream_t stream);
 hipError_t launch_probe_read(const void *buf, size_t bytes, uint32_t *sink,
                              int grid, hipStream_t stream);

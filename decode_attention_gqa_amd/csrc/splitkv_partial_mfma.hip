@@ -251,13 +251,20 @@ __device__ __forceinline__ void compute_tile(
   }
 }
 
-template <int HD, int G>
+// PER_HEAD = false: one workgroup per (split, KV head, sequence) computes all
+// G query heads of the group (blockIdx.y = KV head). PER_HEAD = true (with
+// G = 1): one workgroup per (split, query head, sequence), blockIdx.y = query
+// head, reading KV head blockIdx.y / a.kv_group -- the per-query-head grid,
+// kept as an A/B baseline; every KV row is then read once per query head.
+template <int HD, int G, bool PER_HEAD = false>
 __global__ __launch_bounds__(kThreads, HD >= 256 ? 1 : 2) void
 partial_mfma_kernel(PartialArgs a) {
   using Geo = MGeo<HD>;
   static_assert(G >= 1 && G <= 8, "group");
+  static_assert(!PER_HEAD || G == 1, "per-head form computes one head");
   const int sp = blockIdx.x;
-  const int hk = blockIdx.y;
+  const int hy = blockIdx.y;                         // first query head / G
+  const int hk = PER_HEAD ? hy / a.kv_group : hy;    // KV head
   const int b = blockIdx.z;
   const int tid = threadIdx.x;
   // wave index, provably uniform (scalar) so per-tile row math stays scalar
@@ -315,7 +322,7 @@ partial_mfma_kernel(PartialArgs a) {
     const int gq = col & 7;
     float4 qraw[Geo::KS][2];
     {
-      const float *qrow = a.q + ((size_t)b * a.n_head + (size_t)hk * G +
+      const float *qrow = a.q + ((size_t)b * a.n_head + (size_t)hy * G +
                                  (gq < G ? gq : 0)) * HD + 8 * grp;
 #pragma unroll
       for (int ks = 0; ks < Geo::KS; ++ks) {
@@ -333,9 +340,13 @@ partial_mfma_kernel(PartialArgs a) {
                           qraw[ks][1].z, qraw[ks][1].w};
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float v = (gq < G) ? x[e] * a.scale_log2 : 0.0f;
-        const _Float16 h = (_Float16)v;
-        qf[ks][e] = hi_col ? h : (_Float16)(v - (float)h);
+        // q' = q * scale_log2 as hi + lo: hi = fp16(q'), lo = fp16 of the
+        // exact product minus hi (an explicit fma, so every instantiation
+        // rounds the same way whatever the compiler contracts).
+        const _Float16 h = (_Float16)(x[e] * a.scale_log2);
+        const float lo = __builtin_fmaf(x[e], a.scale_log2, -(float)h);
+        const _Float16 val = hi_col ? h : (_Float16)lo;
+        qf[ks][e] = (gq < G) ? val : (_Float16)0.0f;
       }
     }
 
@@ -397,7 +408,7 @@ partial_mfma_kernel(PartialArgs a) {
   constexpr int D4 = HD / 4;
   const size_t pstr = 4 + HD;
   float *rec0 = a.partials +
-                (((size_t)b * a.n_splits + sp) * a.n_head + (size_t)hk * G) *
+                (((size_t)b * a.n_splits + sp) * a.n_head + (size_t)hy * G) *
                     pstr;
   for (int idx = tid; idx < G * D4; idx += kThreads) {
     const int gg = idx / D4;
@@ -451,7 +462,25 @@ hipError_t launch_hd(int group, const PartialArgs &a, int batch,
   }
 }
 
+template <int HD>
+hipError_t launch_per_head(const PartialArgs &a, int batch, hipStream_t stream) {
+  hipLaunchKernelGGL((partial_mfma_kernel<HD, 1, true>),
+                     dim3(a.n_splits, a.n_head, batch), dim3(kThreads), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_partial_per_head(int head_dim, const PartialArgs &a,
+                                   int batch, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return launch_per_head<64>(a, batch, stream);
+    case 128: return launch_per_head<128>(a, batch, stream);
+    case 256: return launch_per_head<256>(a, batch, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 hipError_t launch_partial_mfma(int head_dim, int group, const PartialArgs &a,
                                int batch, hipStream_t stream) {

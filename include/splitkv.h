@@ -113,7 +113,7 @@ int splitkv_workgroups_per_cu(int head_dim, int group);
  *          to the host) about 16 workgroups per compute unit balance uneven
  *          lengths;
  *   n_splits = min(max(fill, bal, 1), max(max_ctx / 32, 1), 65535): a
- *          full-length split keeps at least two 16-row tiles.
+ *          full-length split keeps at least 32 rows (one wave's tile).
  * Host only; returns SPLITKV_OK or a negative status. */
 int splitkv_pick_splits(int batch, int n_head, int n_kv_head, int head_dim,
                         int max_ctx, int cu_count, int *n_splits,
@@ -125,6 +125,22 @@ int splitkv_partial(const float *q, const uint16_t *k_cache,
                     float *partials, int batch, int n_head, int n_kv_head,
                     int head_dim, int max_ctx, int n_splits, int block_len,
                     float scale, void *stream);
+
+/* Partial kernel in the per-query-head form: one workgroup per (split, query
+ * head, sequence) on grid dim3(n_splits, n_head, batch), each reading its KV
+ * head's rows on its own ("10 · R4", section 3.2 launches dim3(S, nh);
+ * "Red Lite dev35", Finding: the earlier kernel with one threadgroup per
+ * block and query head read each K/V row once per query head of the group).
+ * Kept as an A/B baseline against splitkv_partial, which reads every row once
+ * per group. Same arguments, records and errors as splitkv_partial; the
+ * records are the same values (each query head's arithmetic is identical).
+ * head_dim 64, 128 and 256 only (else SPLITKV_EUNSUPPORTED). */
+int splitkv_partial_per_head(const float *q, const uint16_t *k_cache,
+                             const uint16_t *v_cache, const int32_t *positions,
+                             float *partials, int batch, int n_head,
+                             int n_kv_head, int head_dim, int max_ctx,
+                             int n_splits, int block_len, float scale,
+                             void *stream);
 
 /* Combine kernel only: merges the records into `out` ("10 · R4", section 2.1:
  * gmx = max mx, w = exp(mx - gmx), o = sum w*oc / sum w*S, 0 when the weight

@@ -61,12 +61,12 @@ def test_pick_splits_properties(lib):
         assert 1 <= S <= 65535 and blk >= 0
         if blk:
             assert blk * S >= T
-        # never so many splits that a full-length split is under two tiles
+        # never so many splits that a full-length split is under one tile
         assert S == 1 or T // S >= 32
     # Values the rule gives on 256 compute units. One sequence: one full round
     # of resident workgroups (2 per compute unit at hd128 -> 128 splits over 4
     # KV heads; 1 at hd256 -> 128 over 2), capped so a full-length split
-    # keeps two 16-row tiles (2048 / 32 -> 64; 256 / 32 -> 8). Batches: ~16
+    # keeps one 32-row tile (2048 / 32 -> 64; 256 / 32 -> 8). Batches: ~16
     # workgroups per compute unit, splits of >= 1024 rows.
     cases = {(1, 28, 4, 128, 33024): 128, (1, 28, 4, 128, 2048): 64,
              (1, 16, 2, 256, 8400): 128, (32, 32, 8, 128, 32768): 16,
@@ -167,6 +167,17 @@ def test_partial_rejects(lib, what, over, code):
     a = _partial_args(**over)
     assert _call_partial(lib, a) == code
     assert _call_decode(lib, a) == code
+
+
+@cpu_only
+@pytest.mark.parametrize("what,over,code", BAD_PARTIAL + [
+    ("head_dim 32 (vector-ALU family)", dict(hd=32), EUNSUP)],
+    ids=[c[0] for c in BAD_PARTIAL] + ["head_dim 32"])
+def test_partial_per_head_rejects(lib, what, over, code):
+    a = _partial_args(**over)
+    assert lib.splitkv_partial_per_head(
+        a["q"], a["k"], a["v"], a["pos"], a["part"], a["B"], a["nh"],
+        a["nkvh"], a["hd"], a["T"], a["S"], a["blk"], a["scale"], None) == code
 
 
 @cpu_only
