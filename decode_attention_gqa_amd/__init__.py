@@ -20,8 +20,8 @@ import os
 import threading
 
 __all__ = ["SplitKVError", "load", "abi_version", "strerror", "partials_bytes",
-           "pick_splits", "partial", "partial_per_head", "combine",
-           "decode_attn", "append_kv",
+           "pick_splits", "partial", "partial_per_head", "partial_rows",
+           "combine", "decode_attn", "decode_attn_rows", "append_kv",
            "workgroups_per_cu", "probe_read",
            "probe_copy", "LIB_PATH", "SUPPORTED_HEAD_DIMS", "MAX_GROUP"]
 
@@ -49,6 +49,10 @@ SIGNATURES = {
                                  ctypes.POINTER(_i), ctypes.POINTER(_i)]),
     "splitkv_partial": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
                              _i, _f, _vp]),
+    "splitkv_partial_rows": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
+                                  _i, _i, _i, _f, _vp]),
+    "splitkv_decode_attn_rows": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i,
+                                      _i, _i, _i, _i, _i, _f, _vp]),
     "splitkv_partial_per_head": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
                                       _i, _i, _i, _f, _vp]),
     "splitkv_combine": (_i, [_vp, _vp, _i, _i, _i, _i, _vp]),
@@ -188,6 +192,58 @@ def partial(q, k_cache, v_cache, positions, partials, n_splits: int,
         q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
         positions.data_ptr(), partials.data_ptr(), B, nh, nkvh, hd, max_ctx,
         n_splits, block_len, scale, _stream_ptr(stream)), "splitkv_partial")
+
+
+def _rows_shapes(q, k_cache, v_cache, positions):
+    torch = _torch()
+    _need(q, (torch.float32,), "q")
+    if q.dim() != 4:
+        raise ValueError("q must be [B][n_q][n_head][hd]")
+    B, n_q, nh, hd = q.shape
+    _need(k_cache, (torch.float16, torch.int16, torch.uint16), "k_cache")
+    _need(v_cache, (torch.float16, torch.int16, torch.uint16), "v_cache")
+    _need(positions, (torch.int32,), "positions")
+    if k_cache.dim() != 4:
+        raise ValueError("k_cache must be [B][max_ctx][n_kv_head][hd]")
+    kb, max_ctx, nkvh, khd = k_cache.shape
+    if kb != B or khd != hd or tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("q, k_cache and v_cache shapes disagree")
+    if positions.numel() != B:
+        raise ValueError("positions must hold one entry per sequence")
+    return B, n_q, nh, nkvh, hd, max_ctx
+
+
+def partial_rows(q, k_cache, v_cache, positions, partials, n_splits: int,
+                 block_len: int = 0, scale: float | None = None, stream=None):
+    """Partial kernel for several query rows per sequence (q [B][n_q][nh][hd],
+    causal within the rows; records [B][S][n_q*nh][4+hd])."""
+    B, n_q, nh, nkvh, hd, max_ctx = _rows_shapes(q, k_cache, v_cache, positions)
+    _partials_ok(partials, B, n_q * nh, hd, n_splits)
+    scale = 1.0 / math.sqrt(hd) if scale is None else float(scale)
+    _check(load().splitkv_partial_rows(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        positions.data_ptr(), partials.data_ptr(), B, n_q, nh, nkvh, hd,
+        max_ctx, n_splits, block_len, scale, _stream_ptr(stream)),
+        "splitkv_partial_rows")
+
+
+def decode_attn_rows(q, k_cache, v_cache, positions, partials, out,
+                     n_splits: int, block_len: int = 0,
+                     scale: float | None = None, stream=None):
+    """Several query rows per sequence: partial then combine; out
+    [B][n_q][n_head][hd]."""
+    torch = _torch()
+    B, n_q, nh, nkvh, hd, max_ctx = _rows_shapes(q, k_cache, v_cache, positions)
+    _partials_ok(partials, B, n_q * nh, hd, n_splits)
+    _need(out, (torch.float32,), "out")
+    if tuple(out.shape) != (B, n_q, nh, hd):
+        raise ValueError("out must be [B][n_q][n_head][hd]")
+    scale = 1.0 / math.sqrt(hd) if scale is None else float(scale)
+    _check(load().splitkv_decode_attn_rows(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        positions.data_ptr(), partials.data_ptr(), out.data_ptr(), B, n_q, nh,
+        nkvh, hd, max_ctx, n_splits, block_len, scale, _stream_ptr(stream)),
+        "splitkv_decode_attn_rows")
 
 
 def partial_per_head(q, k_cache, v_cache, positions, partials, n_splits: int,

@@ -83,7 +83,7 @@ int do_partial(const float *q, const uint16_t *k, const uint16_t *v,
                const int32_t *positions, float *partials, int batch,
                int n_head, int n_kv_head, int head_dim, int max_ctx,
                int n_splits, int block_len, float scale, void *stream,
-               bool per_head = false) {
+               bool per_head = false, int n_q = 1) {
   splitkv::PartialArgs a;
   a.q = q;
   a.k = k;
@@ -97,6 +97,7 @@ int do_partial(const float *q, const uint16_t *k, const uint16_t *v,
   a.block_len = block_len;
   a.scale_log2 = (float)((double)scale * kLog2e);
   a.kv_group = n_head / n_kv_head;
+  a.n_q = n_q;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e =
       per_head ? splitkv::launch_partial_per_head(head_dim, a, batch, s)
@@ -229,6 +230,46 @@ int splitkv_decode_attn(const float *q, const uint16_t *k_cache,
                   stream);
   if (st != SPLITKV_OK) return st;
   return do_combine(partials, out, batch, n_head, head_dim, n_splits, stream);
+}
+
+int splitkv_partial_rows(const float *q, const uint16_t *k_cache,
+                         const uint16_t *v_cache, const int32_t *positions,
+                         float *partials, int batch, int n_q, int n_head,
+                         int n_kv_head, int head_dim, int max_ctx, int n_splits,
+                         int block_len, float scale, void *stream) {
+  const int st = check_partial(q, k_cache, v_cache, positions, partials, batch,
+                               n_head, n_kv_head, head_dim, max_ctx, n_splits,
+                               block_len, scale);
+  if (st != SPLITKV_OK) return st;
+  if (n_q < 1 || (long long)batch * n_q > kMaxGridYZ ||
+      (long long)n_q * n_head > kMaxGridYZ)
+    return SPLITKV_EINVAL;
+  return do_partial(q, k_cache, v_cache, positions, partials, batch, n_head,
+                    n_kv_head, head_dim, max_ctx, n_splits, block_len, scale,
+                    stream, false, n_q);
+}
+
+int splitkv_decode_attn_rows(const float *q, const uint16_t *k_cache,
+                             const uint16_t *v_cache, const int32_t *positions,
+                             float *partials, float *out, int batch, int n_q,
+                             int n_head, int n_kv_head, int head_dim,
+                             int max_ctx, int n_splits, int block_len,
+                             float scale, void *stream) {
+  int st = check_partial(q, k_cache, v_cache, positions, partials, batch,
+                         n_head, n_kv_head, head_dim, max_ctx, n_splits,
+                         block_len, scale);
+  if (st != SPLITKV_OK) return st;
+  if (n_q < 1 || (long long)batch * n_q > kMaxGridYZ ||
+      (long long)n_q * n_head > kMaxGridYZ)
+    return SPLITKV_EINVAL;
+  st = check_combine(partials, out, batch, n_q * n_head, head_dim, n_splits);
+  if (st != SPLITKV_OK) return st;
+  st = do_partial(q, k_cache, v_cache, positions, partials, batch, n_head,
+                  n_kv_head, head_dim, max_ctx, n_splits, block_len, scale,
+                  stream, false, n_q);
+  if (st != SPLITKV_OK) return st;
+  return do_combine(partials, out, batch, n_q * n_head, head_dim, n_splits,
+                    stream);
 }
 
 int splitkv_partial_per_head(const float *q, const uint16_t *k_cache,

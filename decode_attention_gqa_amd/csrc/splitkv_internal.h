@@ -10,11 +10,11 @@ namespace splitkv {
 
 // Arguments of the partial kernel, passed by value.
 struct PartialArgs {
-  const float *q;            // [B][n_head][HD] fp32
+  const float *q;            // [B][n_q][n_head][HD] fp32
   const uint16_t *k;         // [B][max_ctx][n_kv_head][HD] fp16 bits
   const uint16_t *v;         // same layout
   const int32_t *positions;  // [B]
-  float *partials;           // [B][n_splits][n_head][4 + HD]
+  float *partials;           // [B][n_splits][n_q * n_head][4 + HD]
   int n_head;
   int n_kv_head;
   int max_ctx;
@@ -22,6 +22,8 @@ struct PartialArgs {
   int block_len;             // 0: chunk = ceil(nkv / n_splits)
   float scale_log2;          // scale * log2(e): scores are kept in base-2 units
   int kv_group;              // per-query-head form only: n_head / n_kv_head
+  int n_q;                   // query rows per sequence (1: one-token decode);
+                             // grid z = batch * n_q, one row per workgroup
 };
 
 struct CombineArgs {

@@ -53,6 +53,51 @@ __device__ __forceinline__ SplitRange split_range(const PartialArgs &a,
   return r;
 }
 
+// The (sequence, query row) a partial workgroup serves: blockIdx.z =
+// b * n_q + t. With several query rows ("dotLLM issue #199", comment 1,
+// section 2: seqQ > 1 with a causal mask from positionOffset) row t sits at
+// position positions[b] - (n_q - 1 - t) and sees the cache rows before and
+// at it: its live length is clamp(positions[b] + 1 - (n_q - 1 - t), 0,
+// max_ctx). The splits are those of the last row (live length nkv_b), the
+// same for every row, and row t stops at min(hi, its live length).
+struct RowSel {
+  int b;
+  int t;
+};
+__device__ __forceinline__ RowSel row_sel(const PartialArgs &a) {
+  RowSel r;
+  if (a.n_q == 1) {
+    r.b = blockIdx.z;
+    r.t = 0;
+  } else {
+    r.b = blockIdx.z / a.n_q;
+    r.t = blockIdx.z - r.b * a.n_q;
+  }
+  return r;
+}
+
+// End of query row t's rows within the split [lo, hi).
+__device__ __forceinline__ long long row_end(const PartialArgs &a,
+                                             const RowSel &rs, long long hi) {
+  if (a.n_q == 1) return hi;  // the one row is the last row: nkv_b >= hi
+  long long n = (long long)a.positions[rs.b] + 1 - (a.n_q - 1 - rs.t);
+  n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
+  return n < hi ? n : hi;
+}
+
+// Offsets of query row t of sequence b: its first q element and its first
+// record ([B][S][n_q * n_head][4 + HD], record head index t * n_head + h).
+__device__ __forceinline__ size_t q_offset(const PartialArgs &a,
+                                           const RowSel &rs, int head, int hd) {
+  return (((size_t)rs.b * a.n_q + rs.t) * a.n_head + head) * (size_t)hd;
+}
+__device__ __forceinline__ size_t rec_offset(const PartialArgs &a,
+                                             const RowSel &rs, int sp,
+                                             int head, int hd) {
+  return ((((size_t)rs.b * a.n_splits + sp) * a.n_q + rs.t) * a.n_head +
+          head) * (size_t)(4 + hd);
+}
+
 // Merge (m2, s2) into (m, s) and return the weights (c1, c2) applied to the
 // two accumulators; base-2 units; a -inf state has weight exactly 0.
 struct MergeW {
@@ -77,13 +122,11 @@ __device__ __forceinline__ MergeW merge_weights(float &m, float &s, float m2,
 // KV head hk. Must be called by all threads after a barrier.
 template <int HD, int G>
 __device__ __forceinline__ void write_records(
-    const PartialArgs &a, int sp, int hk, int b, const SplitRange &rg,
-    const float (&sm_m)[kWaves][G], const float (&sm_s)[kWaves][G],
-    const float (&sm_o)[kWaves][G][HD]) {
+    const PartialArgs &a, int sp, int hk, const RowSel &rs,
+    const SplitRange &rg, const float (&sm_m)[kWaves][G],
+    const float (&sm_s)[kWaves][G], const float (&sm_o)[kWaves][G][HD]) {
   const size_t pstr = 4 + HD;
-  float *rec0 = a.partials +
-                (((size_t)b * a.n_splits + sp) * a.n_head + (size_t)hk * G) *
-                    pstr;
+  float *rec0 = a.partials + rec_offset(a, rs, sp, hk * G, HD);
   for (int idx = threadIdx.x; idx < G * HD; idx += kThreads) {
     const int g = idx / HD;
     const int d = idx % HD;

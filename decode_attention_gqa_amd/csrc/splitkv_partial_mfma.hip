@@ -265,7 +265,8 @@ partial_mfma_kernel(PartialArgs a) {
   const int sp = blockIdx.x;
   const int hy = blockIdx.y;                         // first query head / G
   const int hk = PER_HEAD ? hy / a.kv_group : hy;    // KV head
-  const int b = blockIdx.z;
+  const detail::RowSel rs = detail::row_sel(a);      // (sequence, query row)
+  const int b = rs.b;
   const int tid = threadIdx.x;
   // wave index, provably uniform (scalar) so per-tile row math stays scalar
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -279,10 +280,11 @@ partial_mfma_kernel(PartialArgs a) {
   __shared__ float sm_s[kWaves][G];
   __shared__ __attribute__((aligned(16))) float sm_o[kWaves][G][HD];
 
-  // a1 + a2: live length and this split's rows.
+  // a1 + a2: live length and this split's rows; with several query rows,
+  // this row's rows end at min(hi, its own live length).
   const detail::SplitRange rg = detail::split_range(a, sp, b);
   const long long lo = rg.lo;
-  const long long hi = rg.hi;
+  const long long hi = detail::row_end(a, rs, rg.hi);
 
   // This (sequence, KV head) slice of the caches: row r at byte r * row_bytes.
   const uint32_t row_bytes = (uint32_t)(a.n_kv_head * HD * 2);
@@ -322,8 +324,9 @@ partial_mfma_kernel(PartialArgs a) {
     const int gq = col & 7;
     float4 qraw[Geo::KS][2];
     {
-      const float *qrow = a.q + ((size_t)b * a.n_head + (size_t)hy * G +
-                                 (gq < G ? gq : 0)) * HD + 8 * grp;
+      const float *qrow =
+          a.q + detail::q_offset(a, rs, hy * G + (gq < G ? gq : 0), HD) +
+          8 * grp;
 #pragma unroll
       for (int ks = 0; ks < Geo::KS; ++ks) {
         qraw[ks][0] = *reinterpret_cast<const float4 *>(qrow + 32 * ks);
@@ -407,9 +410,7 @@ partial_mfma_kernel(PartialArgs a) {
   __syncthreads();
   constexpr int D4 = HD / 4;
   const size_t pstr = 4 + HD;
-  float *rec0 = a.partials +
-                (((size_t)b * a.n_splits + sp) * a.n_head + (size_t)hy * G) *
-                    pstr;
+  float *rec0 = a.partials + detail::rec_offset(a, rs, sp, hy * G, HD);
   for (int idx = tid; idx < G * D4; idx += kThreads) {
     const int gg = idx / D4;
     const int d4 = idx % D4;
@@ -441,8 +442,8 @@ partial_mfma_kernel(PartialArgs a) {
 template <int HD, int G>
 hipError_t launch_one(const PartialArgs &a, int batch, hipStream_t stream) {
   hipLaunchKernelGGL((partial_mfma_kernel<HD, G>),
-                     dim3(a.n_splits, a.n_kv_head, batch), dim3(kThreads), 0,
-                     stream, a);
+                     dim3(a.n_splits, a.n_kv_head, batch * a.n_q),
+                     dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

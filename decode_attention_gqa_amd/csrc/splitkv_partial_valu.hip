@@ -106,7 +106,8 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(PartialArgs a) {
 
   const int sp = blockIdx.x;
   const int hk = blockIdx.y;
-  const int b = blockIdx.z;
+  const detail::RowSel rs = detail::row_sel(a);
+  const int b = rs.b;
   const int tid = threadIdx.x;
   const int wave = tid >> 6;
   const int lane = tid & 63;
@@ -114,15 +115,15 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(PartialArgs a) {
   const int li = lane % L;
 
   // a1 + a2: live length (read on the device) and this split's rows.
+  // With several query rows, this row's rows end at min(hi, its length).
   const detail::SplitRange rg = detail::split_range(a, sp, b);
   const long long lo = rg.lo;
-  const long long hi = rg.hi;
+  const long long hi = detail::row_end(a, rs, rg.hi);
 
   // a3: the group's queries, this lane's 8 dims, pre-scaled to base-2 units.
   float qv[G][8];
   {
-    const float *qb =
-        a.q + ((size_t)b * a.n_head + (size_t)hk * G) * HD + li * 8;
+    const float *qb = a.q + detail::q_offset(a, rs, hk * G, HD) + li * 8;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const float4 x0 = *reinterpret_cast<const float4 *>(qb + g * HD);
@@ -236,13 +237,14 @@ __global__ __launch_bounds__(kThreads) void partial_valu_kernel(PartialArgs a) {
   }
   __syncthreads();
 
-  detail::write_records<HD, G>(a, sp, hk, b, rg, sm_mx, sm_s, sm_acc);
+  detail::write_records<HD, G>(a, sp, hk, rs, rg, sm_mx, sm_s, sm_acc);
 }
 
 template <int HD, int G>
 hipError_t launch_one(const PartialArgs &a, int batch, hipStream_t stream) {
   hipLaunchKernelGGL((partial_valu_kernel<HD, G>),
-                     dim3(a.n_splits, a.n_kv_head, batch), dim3(kThreads), 0,
+                     dim3(a.n_splits, a.n_kv_head, batch * a.n_q),
+                     dim3(kThreads), 0,
                      stream, a);
   return hipGetLastError();
 }

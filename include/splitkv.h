@@ -126,6 +126,41 @@ int splitkv_partial(const float *q, const uint16_t *k_cache,
                     int head_dim, int max_ctx, int n_splits, int block_len,
                     float scale, void *stream);
 
+/* Several query rows per sequence (dotLLM issue #199, comment 1, section 2:
+ * seqQ > 1 for speculative verification or chunked prefill, with the causal
+ * mask taken from positionOffset). Row t = 0..n_q-1 of sequence b sits at
+ * position positions[b] - (n_q - 1) + t, the last row at positions[b]
+ * (positionOffset = positions[b] - n_q + 1); row t attends
+ * to the cache rows 0 .. its own position (clamped to [0, max_ctx)), so each
+ * row is exactly a one-row decode at its position, and a row before position
+ * 0 gives 0. The new rows' K/V must already be in the cache
+ * (splitkv_append_kv with n_rows = n_q does that).
+ *   q         device fp32 [batch][n_q][n_head][head_dim], 16-byte aligned.
+ *   partials  splitkv_partials_bytes(batch, n_q * n_head, head_dim,
+ *             n_splits) bytes; records [batch][n_splits][n_q * n_head]
+ *             [4 + head_dim], record head index t * n_head + h, slots [2],
+ *             [3] the split's bounds (those of the last row's live length).
+ *   out       device fp32 [batch][n_q][n_head][head_dim].
+ * The splits are cut from the last row's live length positions[b] + 1, as
+ * for one row; row t's rows end at min(hi, its live length). One partial
+ * workgroup per (split, KV head, sequence, row): grid dim3(n_splits,
+ * n_kv_head, batch * n_q). Other arguments and errors as for
+ * splitkv_partial / splitkv_decode_attn, plus SPLITKV_EINVAL when n_q < 1,
+ * batch * n_q > 65535 or n_q * n_head > 65535. n_q = 1 is exactly
+ * splitkv_partial / splitkv_decode_attn. The combine of these records is
+ * splitkv_combine with n_head -> n_q * n_head. */
+int splitkv_partial_rows(const float *q, const uint16_t *k_cache,
+                         const uint16_t *v_cache, const int32_t *positions,
+                         float *partials, int batch, int n_q, int n_head,
+                         int n_kv_head, int head_dim, int max_ctx, int n_splits,
+                         int block_len, float scale, void *stream);
+int splitkv_decode_attn_rows(const float *q, const uint16_t *k_cache,
+                             const uint16_t *v_cache, const int32_t *positions,
+                             float *partials, float *out, int batch, int n_q,
+                             int n_head, int n_kv_head, int head_dim,
+                             int max_ctx, int n_splits, int block_len,
+                             float scale, void *stream);
+
 /* Partial kernel in the per-query-head form: one workgroup per (split, query
  * head, sequence) on grid dim3(n_splits, n_head, batch), each reading its KV
  * head's rows on its own ("10 · R4", section 3.2 launches dim3(S, nh);

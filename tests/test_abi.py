@@ -250,3 +250,21 @@ def test_append_rejects(lib, what, over, code):
     assert lib.splitkv_append_kv(a["kn"], a["vn"], a["kc"], a["vc"], a["pos"],
                                  a["B"], a["n"], a["nkvh"], a["hd"], a["T"],
                                  None) == code
+
+
+@cpu_only
+@pytest.mark.parametrize("what,over,code", BAD_PARTIAL + [
+    ("n_q 0", dict(nq=0), EINVAL),
+    ("batch * n_q too big", dict(B=300, nq=300), EINVAL),
+    ("n_q * n_head too big", dict(nq=3000, nh=28), EINVAL)],
+    ids=[c[0] for c in BAD_PARTIAL] + ["n_q 0", "grid z", "records per row"])
+def test_rows_reject(lib, what, over, code):
+    a = _partial_args(**{k: v for k, v in over.items() if k != "nq"})
+    nq = over.get("nq", 2)
+    assert lib.splitkv_partial_rows(
+        a["q"], a["k"], a["v"], a["pos"], a["part"], a["B"], nq, a["nh"],
+        a["nkvh"], a["hd"], a["T"], a["S"], a["blk"], a["scale"], None) == code
+    assert lib.splitkv_decode_attn_rows(
+        a["q"], a["k"], a["v"], a["pos"], a["part"], A + 0x5000, a["B"], nq,
+        a["nh"], a["nkvh"], a["hd"], a["T"], a["S"], a["blk"], a["scale"],
+        None) == code
