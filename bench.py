@@ -28,6 +28,7 @@ Usage: python bench.py [--steps K] [--warmup W] [--nkv N] [--layers L]
        python bench.py --mode step      # append + partial + combine per layer
        python bench.py --mode per_head --sweep-splits 18 36 64 128
                                         # grouped vs per-query-head grid
+       python bench.py --mode rows      # n_q query rows per sequence (causal)
        python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --kernels-json F
                                         # fold two rocprofv3 --pmc runs
 """
@@ -679,6 +680,59 @@ def run_per_head(args):
         torch.cuda.empty_cache()
 
 
+def run_rows(args):
+    """Several query rows per sequence (speculative verification shape):
+    28q/4kv hd128, 28 layers of partial + combine in one graph, n_q rows per
+    sequence at several live lengths. The split count comes from the
+    heuristic with batch * n_q workgroup rows."""
+    import torch
+
+    import decode_attention_gqa_amd as skv
+    import synth
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    max_ctx = synth.CFG3.max_ctx
+    base = Layers(args.layers, max_ctx, 1, 0)
+    dev = torch.device("cuda", 0)
+    g = torch.Generator(device=dev)
+    g.manual_seed(4)
+    for n_q in args.rows:
+        S, blk = skv.pick_splits(n_q, 28, 4, 128, max_ctx, cu)
+        qs = [torch.randn((1, n_q, 28, 128), generator=g, device=dev)
+              for _ in range(base.L)]
+        parts = [torch.empty(skv.partials_bytes(1, n_q * 28, 128, S) // 4,
+                             device=dev) for _ in range(base.L)]
+        outs = [torch.empty((1, n_q, 28, 128), device=dev)
+                for _ in range(base.L)]
+
+        def step():
+            for l in range(base.L):
+                skv.decode_attn_rows(qs[l], base.k[l], base.v[l], base.pos,
+                                     parts[l], outs[l], S, blk, base.scale)
+
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        for nkv in args.points:
+            base.set_nkv(nkv)
+            per, _, _ = time_replays(torch, graph, args.warmup, args.steps)
+            med = statistics.median(per)
+            kv = synth.kv_bytes(4, 128, nkv) * base.L
+            print(json.dumps({"rows": n_q, "n_splits": S, "nkv": nkv,
+                              "us_per_layer": round(med * 1e3 / base.L, 3),
+                              "us_per_row_layer": round(med * 1e3 / base.L / n_q, 3),
+                              "kv_gbps_once": round(kv / (med * 1e-3) / 1e9, 1)}),
+                  flush=True)
+        del graph, qs, parts, outs
+        torch.cuda.empty_cache()
+
+
 def run_sweep(args):
     import torch
 
@@ -778,9 +832,11 @@ def main():
     ap.add_argument("--kernels-json", default=None)
     ap.add_argument("--write-traffic", default=None)
     ap.add_argument("--mode", choices=["main", "kernels", "ragged", "configs",
-                                       "oracle", "step", "per_head"],
+                                       "oracle", "step", "per_head", "rows"],
                     default="main")
     ap.add_argument("--ragged-batch", type=int, default=32)
+    ap.add_argument("--rows", type=int, nargs="*", default=[1, 2, 4, 8],
+                    help="--mode rows: query rows per sequence to time")
     ap.add_argument("--per-head", action="store_true",
                     help="--mode kernels: time the per-query-head partial form")
     ap.add_argument("--extra-splits", type=int, nargs="*", default=[],
@@ -812,6 +868,8 @@ def main():
         run_step(args)
     elif args.mode == "per_head":
         run_per_head(args)
+    elif args.mode == "rows":
+        run_rows(args)
     else:
         run_main(args)
     return 0
