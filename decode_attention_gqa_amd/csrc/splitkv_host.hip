@@ -153,7 +153,7 @@ int splitkv_workgroups_per_cu(int head_dim, int group) {
     case 8: { static const int t[8] = {4, 4, 3, 3, 2, 2, 2, 2}; return t[group - 1]; }
     case 16: { static const int t[8] = {4, 3, 3, 2, 2, 2, 2, 1}; return t[group - 1]; }
     case 32: { static const int t[8] = {4, 3, 3, 2, 2, 2, 2, 1}; return t[group - 1]; }
-    case 64: return group == 1 ? 3 : 4;
+    case 64: return 4;
     case 128: return 2;
     case 256: return 1;
     default: return 0;

@@ -60,6 +60,7 @@ typedef __attribute__((address_space(3))) short4v lds_short4v;
 
 constexpr int kTileRows = 32;
 constexpr int kRor8 = 0x128;  // DPP row_ror:8 (rotate by 8 within 16 lanes)
+constexpr float kLazyLog2 = 8.0f;  // reference-max lag allowed (base-2 units)
 
 template <int HD>
 struct MGeo {
@@ -90,6 +91,46 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// x + (x of the lane 8 places along, within each row of 16): the hi + lo
+// column sum. All lanes are valid sources for a rotation, so the move is
+// written with bound_ctrl set, which lets the compiler fold it into the add
+// as a DPP operand.
+__device__ __forceinline__ float add_ror8(float x) {
+  return x + __builtin_bit_cast(
+                 float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x),
+                                                    kRor8, 0xF, 0xF, true));
+}
+
+// Reductions across the four 16-lane rows of a wave (the 4 row groups of an
+// MFMA column). v_permlane16_swap / v_permlane32_swap given (x, x) return, in
+// every lane, the pair (x of the partner lane with that bit clear, x of the
+// one with it set): a VALU exchange instead of an LDS permute round trip, and
+// both lanes of a pair combine the two values in the same order.
+__device__ __forceinline__ float pair16_max(float x) {
+  const int b = __builtin_bit_cast(int, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  return fmaxf(__builtin_bit_cast(float, (int)r[0]),
+               __builtin_bit_cast(float, (int)r[1]));
+}
+__device__ __forceinline__ float pair32_max(float x) {
+  const int b = __builtin_bit_cast(int, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return fmaxf(__builtin_bit_cast(float, (int)r[0]),
+               __builtin_bit_cast(float, (int)r[1]));
+}
+__device__ __forceinline__ float pair16_sum(float x) {
+  const int b = __builtin_bit_cast(int, x);
+  const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+  return __builtin_bit_cast(float, (int)r[0]) +
+         __builtin_bit_cast(float, (int)r[1]);
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+  const int b = __builtin_bit_cast(int, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+  return __builtin_bit_cast(float, (int)r[0]) +
+         __builtin_bit_cast(float, (int)r[1]);
 }
 
 constexpr int kBufferWord3 = 0x00020000;  // gfx9-family raw buffer format
@@ -160,7 +201,8 @@ template <int HD>
 __device__ __forceinline__ void compute_tile(
     const TileRegs<HD> &t, uint32_t tb, uint32_t hi,
     const half8 (&qf)[MGeo<HD>::KS], float4v (&oacc)[MGeo<HD>::DB],
-    float &m_run, float &s_run, unsigned char *vlds, int col, int grp,
+    float &m_run, float &m_true, float &s_run, unsigned char *vlds, int col,
+    int grp,
     int lane, bool hi_col) {
   using Geo = MGeo<HD>;
   // a4: scores S = K · Q'ᵀ for the tile's two 16-row groups.
@@ -178,7 +220,7 @@ __device__ __forceinline__ void compute_tile(
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s[rt][r] = sc[rt][r] + dpp_mov<kRor8>(sc[rt][r]);
+    for (int r = 0; r < 4; ++r) s[rt][r] = add_ror8(sc[rt][r]);
   }
   if (tb + kTileRows > hi) {
 #pragma unroll
@@ -194,24 +236,34 @@ __device__ __forceinline__ void compute_tile(
 #pragma unroll
     for (int r = 0; r < 4; ++r) mt = fmaxf(mt, s[rt][r]);
   }
-  mt = fmaxf(mt, __shfl_xor(mt, 16));
-  mt = fmaxf(mt, __shfl_xor(mt, 32));
-  // a5: online softmax. The tile's first row is live, so mn is finite.
-  const float mn = fmaxf(m_run, mt);
+  mt = pair32_max(pair16_max(mt));
+  // a5: online softmax against a reference max m_run that moves only when a
+  // tile's max exceeds it by more than kLazyLog2 (and always from -inf; the
+  // tile's first row is live, so mt is finite). Until then p = exp2(s - m_run)
+  // may exceed 1, up to 2^kLazyLog2, which the fp32 sums and the fp16 hi + lo
+  // split of p carry at full precision; the rescale of the accumulators is
+  // skipped for most tiles. The exact running max m_true is kept beside it,
+  // and the final merge takes every state to m_true, so the records are the
+  // same (max, sum, output) triple as with an exact max at every tile.
+  m_true = fmaxf(m_true, mt);
+  const float mn = (mt > m_run + kLazyLog2) ? mt : m_run;
   const float corr = fast_exp2(m_run - mn);  // 0 while m_run is -inf
   half8 pf;
-  float psum = 0.0f;
+  float pv[8];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float p = fast_exp2(s[rt][r] - mn);  // exp2(-inf) = 0
-      psum += p;
+      pv[4 * rt + r] = p;
       const _Float16 h = (_Float16)p;
       pf[4 * rt + r] = hi_col ? h : (_Float16)(p - (float)h);
     }
   }
-  // Rescale only when some column's running max moved (else corr is 1 for
+  // the tile's weight sum as a tree (no 8-long dependent chain)
+  const float psum = ((pv[0] + pv[1]) + (pv[2] + pv[3])) +
+                     ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+  // Rescale only when some column's reference moved (else corr is 1 for
   // every column and the products would change nothing).
   if (__any(mn != m_run)) {
     s_run *= corr;
@@ -276,7 +328,8 @@ partial_mfma_kernel(PartialArgs a) {
   const bool hi_col = col < 8;
 
   __shared__ __attribute__((aligned(16))) unsigned char sm_v[kWaves * Geo::VTILE];
-  __shared__ float sm_m[kWaves][G];
+  __shared__ float sm_m[kWaves][G];   // each wave's reference max
+  __shared__ float sm_t[kWaves][G];   // each wave's exact max
   __shared__ float sm_s[kWaves][G];
   __shared__ __attribute__((aligned(16))) float sm_o[kWaves][G][HD];
 
@@ -301,7 +354,8 @@ partial_mfma_kernel(PartialArgs a) {
   float4v oacc[Geo::DB];
 #pragma unroll
   for (int i = 0; i < Geo::DB; ++i) oacc[i] = float4v{0.f, 0.f, 0.f, 0.f};
-  float m_run = neg_inf();
+  float m_run = neg_inf();   // reference max (base-2 units), see compute_tile
+  float m_true = neg_inf();  // exact running max
   float s_run = 0.0f;
 
   // A wave whose first tile starts at or past hi has no rows: it keeps the
@@ -362,7 +416,7 @@ partial_mfma_kernel(PartialArgs a) {
       // invariant: ta holds tile t0, tb holds tile t0 + step
       while (true) {
         const uint32_t t1 = t0 + step;
-        compute_tile<HD>(ta, t0, hi32, qf, oacc, m_run, s_run, vlds, col, grp,
+        compute_tile<HD>(ta, t0, hi32, qf, oacc, m_run, m_true, s_run, vlds, col, grp,
                          lane, hi_col);
         if (t1 >= hi32) break;
         // Inside the loop the next tile is loaded only if it has rows: even
@@ -370,7 +424,7 @@ partial_mfma_kernel(PartialArgs a) {
         // a few tiles.
         if (t1 + step < hi32)
           load_tile<HD>(ta, kseq, vseq, row_bytes, t1 + step, hi32, lo_off);
-        compute_tile<HD>(tb, t1, hi32, qf, oacc, m_run, s_run, vlds, col, grp,
+        compute_tile<HD>(tb, t1, hi32, qf, oacc, m_run, m_true, s_run, vlds, col, grp,
                          lane, hi_col);
         t0 = t1 + step;
         if (t0 >= hi32) break;
@@ -379,7 +433,7 @@ partial_mfma_kernel(PartialArgs a) {
       }
     } else {
       while (true) {
-        compute_tile<HD>(ta, t0, hi32, qf, oacc, m_run, s_run, vlds, col, grp,
+        compute_tile<HD>(ta, t0, hi32, qf, oacc, m_run, m_true, s_run, vlds, col, grp,
                          lane, hi_col);
         t0 += step;
         if (t0 >= hi32) break;
@@ -389,20 +443,21 @@ partial_mfma_kernel(PartialArgs a) {
   }
 
   // a6: merge the four waves and write the records. Each wave puts its state
-  // in LDS (max and sum per head; O with the hi and lo columns added), then
-  // after one barrier every thread merges one float4 of one head's output
-  // over the four waves with exact weights exp2(m_wave - m_all).
-  s_run += __shfl_xor(s_run, 16);
-  s_run += __shfl_xor(s_run, 32);
+  // in LDS (reference max, exact max and sum per head; O with the hi and lo
+  // columns added), then after one barrier every thread merges one float4 of
+  // one head's output over the four waves with weights exp2(m_ref - m_all),
+  // m_all the largest exact max: the record is relative to the exact max.
+  s_run = pair32_sum(pair16_sum(s_run));
   if (grp == 0 && col < G) {
     sm_m[wave][col] = m_run;
+    sm_t[wave][col] = m_true;
     sm_s[wave][col] = s_run;
   }
 #pragma unroll
   for (int i = 0; i < Geo::DB; ++i) {
     float o4[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) o4[r] = oacc[i][r] + dpp_mov<kRor8>(oacc[i][r]);
+    for (int r = 0; r < 4; ++r) o4[r] = add_ror8(oacc[i][r]);
     if (col < G)
       *reinterpret_cast<float4 *>(&sm_o[wave][col][16 * i + 4 * grp]) =
           make_float4(o4[0], o4[1], o4[2], o4[3]);
@@ -416,7 +471,7 @@ partial_mfma_kernel(PartialArgs a) {
     const int d4 = idx % D4;
     float mm = neg_inf();
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, sm_m[w][gg]);
+    for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, sm_t[w][gg]);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float st = 0.0f;
 #pragma unroll
