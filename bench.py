@@ -682,26 +682,31 @@ def run_per_head(args):
 
 def run_rows(args):
     """Several query rows per sequence (speculative verification shape):
-    28q/4kv hd128, 28 layers of partial + combine in one graph, n_q rows per
-    sequence at several live lengths. The split count comes from the
-    heuristic with batch * n_q workgroup rows."""
+    28 layers of partial + combine in one graph, n_q rows per sequence at
+    several live lengths, for the head layout given by --rows-heads (query
+    heads, KV heads; hd128). The split count comes from the heuristic with
+    batch * n_q workgroup rows."""
     import torch
 
     import decode_attention_gqa_amd as skv
     import synth
     cu = torch.cuda.get_device_properties(0).multi_processor_count
     max_ctx = synth.CFG3.max_ctx
-    base = Layers(args.layers, max_ctx, 1, 0)
+    nh, nkvh = args.rows_heads
+    sh = synth.Shape(1, nh, nkvh, 128, max_ctx)
+    log(f"[bench] generating layer data: {nh}q/{nkvh}kv max_ctx={max_ctx}")
+    base = Layers(args.layers, max_ctx, 1, 0, sh,
+                  synth.make_case(3, sh, max_ctx))
     dev = torch.device("cuda", 0)
     g = torch.Generator(device=dev)
     g.manual_seed(4)
     for n_q in args.rows:
-        S, blk = skv.pick_splits(n_q, 28, 4, 128, max_ctx, cu)
-        qs = [torch.randn((1, n_q, 28, 128), generator=g, device=dev)
+        S, blk = skv.pick_splits(n_q, nh, nkvh, 128, max_ctx, cu)
+        qs = [torch.randn((1, n_q, nh, 128), generator=g, device=dev)
               for _ in range(base.L)]
-        parts = [torch.empty(skv.partials_bytes(1, n_q * 28, 128, S) // 4,
+        parts = [torch.empty(skv.partials_bytes(1, n_q * nh, 128, S) // 4,
                              device=dev) for _ in range(base.L)]
-        outs = [torch.empty((1, n_q, 28, 128), device=dev)
+        outs = [torch.empty((1, n_q, nh, 128), device=dev)
                 for _ in range(base.L)]
 
         def step():
@@ -723,8 +728,9 @@ def run_rows(args):
             base.set_nkv(nkv)
             per, _, _ = time_replays(torch, graph, args.warmup, args.steps)
             med = statistics.median(per)
-            kv = synth.kv_bytes(4, 128, nkv) * base.L
-            print(json.dumps({"rows": n_q, "n_splits": S, "nkv": nkv,
+            kv = synth.kv_bytes(nkvh, 128, nkv) * base.L
+            print(json.dumps({"heads": f"{nh}q/{nkvh}kv", "rows": n_q,
+                              "n_splits": S, "nkv": nkv,
                               "us_per_layer": round(med * 1e3 / base.L, 3),
                               "us_per_row_layer": round(med * 1e3 / base.L / n_q, 3),
                               "kv_gbps_once": round(kv / (med * 1e-3) / 1e9, 1)}),
@@ -837,6 +843,8 @@ def main():
     ap.add_argument("--ragged-batch", type=int, default=32)
     ap.add_argument("--rows", type=int, nargs="*", default=[1, 2, 4, 8],
                     help="--mode rows: query rows per sequence to time")
+    ap.add_argument("--rows-heads", type=int, nargs=2, default=[28, 4],
+                    help="--mode rows: query heads and KV heads (hd128)")
     ap.add_argument("--per-head", action="store_true",
                     help="--mode kernels: time the per-query-head partial form")
     ap.add_argument("--extra-splits", type=int, nargs="*", default=[],

@@ -13,8 +13,9 @@
 // 16-byte loads and NG = 256/C record groups run side by side; each thread
 // takes every NG-th record, several per pass with all loads issued before the
 // arithmetic, and keeps a running (max, sum, acc) with the same exact
-// re-weighting. The NG partial states are merged by lane shuffles inside each
-// wave and through LDS across the four waves.
+// re-weighting. The NG partial states are merged by lane exchanges inside
+// each wave (a DPP rotation for lanes 8 apart, v_permlane16/32_swap for 16
+// and 32) and through LDS across the four waves.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -33,6 +34,57 @@ __device__ __forceinline__ float neg_inf() { return -__builtin_huge_valf(); }
 // itself -inf (then every x is -inf too).
 __device__ __forceinline__ float weight(float x, float m) {
   return (x == neg_inf()) ? 0.0f : __builtin_amdgcn_exp2f((x - m) * kLog2e);
+}
+
+// One lane's running state: max, weight sum, weighted output slice.
+struct State {
+  float m;
+  float s;
+  float4 acc;
+};
+
+__device__ __forceinline__ float xchg(float x, int off) {
+  const int b = __builtin_bit_cast(int, x);
+  const bool upper = (threadIdx.x & off) != 0;
+  if (off == 32) {
+    // v_permlane32_swap(x, x): every lane gets (x of lane & ~32, x of lane | 32)
+    const auto r = __builtin_amdgcn_permlane32_swap(b, b, false, false);
+    return __builtin_bit_cast(float, (int)(upper ? r[0] : r[1]));
+  }
+  if (off == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(b, b, false, false);
+    return __builtin_bit_cast(float, (int)(upper ? r[0] : r[1]));
+  }
+  if (off == 8)  // rotation by 8 within each row of 16 lanes = lane ^ 8
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_update_dpp(0, b, 0x128, 0xF, 0xF, true));
+  return __shfl_xor(x, off);
+}
+
+// The state of the lane `off` places away (lane ^ off).
+__device__ __forceinline__ State partner(const State &x, int off) {
+  State o;
+  o.m = xchg(x.m, off);
+  o.s = xchg(x.s, off);
+  o.acc.x = xchg(x.acc.x, off);
+  o.acc.y = xchg(x.acc.y, off);
+  o.acc.z = xchg(x.acc.z, off);
+  o.acc.w = xchg(x.acc.w, off);
+  return o;
+}
+
+// Exact merge of two states (weights exp(m_i - max), 0 for an empty state).
+__device__ __forceinline__ void merge(float &m, float &s, float4 &acc,
+                                      const State &o) {
+  const float mn = fmaxf(m, o.m);
+  const float c1 = weight(m, mn);
+  const float c2 = weight(o.m, mn);
+  s = s * c1 + o.s * c2;
+  acc.x = acc.x * c1 + o.acc.x * c2;
+  acc.y = acc.y * c1 + o.acc.y * c2;
+  acc.z = acc.z * c1 + o.acc.z * c2;
+  acc.w = acc.w * c1 + o.acc.w * c2;
+  m = mn;
 }
 
 template <int HD>
@@ -96,26 +148,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   }
 
   // Merge the NG record groups: first across the groups of each wave with
-  // lane shuffles (groups are C lanes apart), then across the waves through
+  // lane exchanges (groups are C lanes apart), then across the waves through
   // LDS. Every lane of a group holds the same (m, s).
 #pragma unroll
   for (int off = C; off < 64; off <<= 1) {
-    const float m2 = __shfl_xor(m, off);
-    const float s2 = __shfl_xor(s, off);
-    float4 a2;
-    a2.x = __shfl_xor(acc.x, off);
-    a2.y = __shfl_xor(acc.y, off);
-    a2.z = __shfl_xor(acc.z, off);
-    a2.w = __shfl_xor(acc.w, off);
-    const float mn = fmaxf(m, m2);
-    const float c1 = weight(m, mn);
-    const float c2 = weight(m2, mn);
-    s = s * c1 + s2 * c2;
-    acc.x = acc.x * c1 + a2.x * c2;
-    acc.y = acc.y * c1 + a2.y * c2;
-    acc.z = acc.z * c1 + a2.z * c2;
-    acc.w = acc.w * c1 + a2.w * c2;
-    m = mn;
+    State o = partner(State{m, s, acc}, off);
+    merge(m, s, acc, o);
   }
   constexpr int kW = kThreads / 64;
   __shared__ float sm_m[kW];

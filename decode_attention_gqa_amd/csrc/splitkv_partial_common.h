@@ -76,13 +76,17 @@ __device__ __forceinline__ RowSel row_sel(const PartialArgs &a) {
   return r;
 }
 
-// End of query row t's rows within the split [lo, hi).
+// End of query row t of sequence b within the split [lo, hi).
+__device__ __forceinline__ long long row_end_at(const PartialArgs &a, int b,
+                                                int t, long long hi) {
+  long long n = (long long)a.positions[b] + 1 - (a.n_q - 1 - t);
+  n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
+  return n < hi ? n : hi;
+}
 __device__ __forceinline__ long long row_end(const PartialArgs &a,
                                              const RowSel &rs, long long hi) {
   if (a.n_q == 1) return hi;  // the one row is the last row: nkv_b >= hi
-  long long n = (long long)a.positions[rs.b] + 1 - (a.n_q - 1 - rs.t);
-  n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
-  return n < hi ? n : hi;
+  return row_end_at(a, rs.b, rs.t, hi);
 }
 
 // Offsets of query row t of sequence b: its first q element and its first

@@ -197,9 +197,13 @@ __device__ __forceinline__ void load_tile(TileRegs<HD> &t, const uint16_t *kseq,
   }
 }
 
-template <int HD>
+// mask_from: wave-uniform row from which some column may be masked; lim: this
+// lane's column's end row (equal to mask_from with one query row per
+// workgroup). SAFE: a column may have no live row yet (several query rows per
+// workgroup), so -inf maxima are guarded.
+template <int HD, bool SAFE>
 __device__ __forceinline__ void compute_tile(
-    const TileRegs<HD> &t, uint32_t tb, uint32_t hi,
+    const TileRegs<HD> &t, uint32_t tb, uint32_t mask_from, uint32_t lim,
     const half8 (&qf)[MGeo<HD>::KS], float4v (&oacc)[MGeo<HD>::DB],
     float &m_run, float &m_true, float &s_run, unsigned char *vlds, int col,
     int grp,
@@ -215,19 +219,20 @@ __device__ __forceinline__ void compute_tile(
       sc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(t.k[rt][ks]),
                                                       qf[ks], sc[rt], 0, 0, 0);
   }
-  // hi + lo columns; rows past the split's end (last tile only) score -inf.
+  // hi + lo columns; rows at or past the column's end (last tiles only) score
+  // -inf.
   float s[2][4];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) s[rt][r] = add_ror8(sc[rt][r]);
   }
-  if (tb + kTileRows > hi) {
+  if (tb + kTileRows > mask_from) {
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        if (tb + (uint32_t)(16 * rt + 4 * grp + r) >= hi) s[rt][r] = neg_inf();
+        if (tb + (uint32_t)(16 * rt + 4 * grp + r) >= lim) s[rt][r] = neg_inf();
     }
   }
   float mt = neg_inf();
@@ -247,14 +252,16 @@ __device__ __forceinline__ void compute_tile(
   // same (max, sum, output) triple as with an exact max at every tile.
   m_true = fmaxf(m_true, mt);
   const float mn = (mt > m_run + kLazyLog2) ? mt : m_run;
-  const float corr = fast_exp2(m_run - mn);  // 0 while m_run is -inf
+  // 0 while m_run is -inf (and with SAFE also while mn still is)
+  const float corr = (SAFE && m_run == neg_inf()) ? 0.0f : fast_exp2(m_run - mn);
+  const float mref = (SAFE && mn == neg_inf()) ? 0.0f : mn;
   half8 pf;
   float pv[8];
 #pragma unroll
   for (int rt = 0; rt < 2; ++rt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const float p = fast_exp2(s[rt][r] - mn);  // exp2(-inf) = 0
+      const float p = fast_exp2(s[rt][r] - mref);  // exp2(-inf) = 0
       pv[4 * rt + r] = p;
       const _Float16 h = (_Float16)p;
       pf[4 * rt + r] = hi_col ? h : (_Float16)(p - (float)h);
@@ -308,16 +315,28 @@ __device__ __forceinline__ void compute_tile(
 // G = 1): one workgroup per (split, query head, sequence), blockIdx.y = query
 // head, reading KV head blockIdx.y / a.kv_group -- the per-query-head grid,
 // kept as an A/B baseline; every KV row is then read once per query head.
-template <int HD, int G, bool PER_HEAD = false>
+// R: query rows per workgroup (several query rows per sequence). The MFMA
+// columns then hold (row, head) pairs, column c = r * G + g, so every K/V row
+// is read once for the R rows; with R = 1 each workgroup serves one row.
+template <int HD, int G, bool PER_HEAD = false, int R = 1>
 __global__ __launch_bounds__(kThreads, HD >= 256 ? 1 : 2) void
 partial_mfma_kernel(PartialArgs a) {
   using Geo = MGeo<HD>;
-  static_assert(G >= 1 && G <= 8, "group");
-  static_assert(!PER_HEAD || G == 1, "per-head form computes one head");
+  constexpr int NC = G * R;                          // MFMA columns in use
+  static_assert(G >= 1 && G <= 8 && NC <= 8, "group x rows");
+  static_assert(!PER_HEAD || (G == 1 && R == 1), "per-head form: one head");
   const int sp = blockIdx.x;
   const int hy = blockIdx.y;                         // first query head / G
   const int hk = PER_HEAD ? hy / a.kv_group : hy;    // KV head
-  const detail::RowSel rs = detail::row_sel(a);      // (sequence, query row)
+  // (sequence, first query row of this workgroup)
+  detail::RowSel rs;
+  if constexpr (R == 1) {
+    rs = detail::row_sel(a);
+  } else {
+    const int nrb = (a.n_q + R - 1) / R;
+    rs.b = blockIdx.z / nrb;
+    rs.t = (blockIdx.z - rs.b * nrb) * R;
+  }
   const int b = rs.b;
   const int tid = threadIdx.x;
   // wave index, provably uniform (scalar) so per-tile row math stays scalar
@@ -328,16 +347,38 @@ partial_mfma_kernel(PartialArgs a) {
   const bool hi_col = col < 8;
 
   __shared__ __attribute__((aligned(16))) unsigned char sm_v[kWaves * Geo::VTILE];
-  __shared__ float sm_m[kWaves][G];   // each wave's reference max
-  __shared__ float sm_t[kWaves][G];   // each wave's exact max
-  __shared__ float sm_s[kWaves][G];
-  __shared__ __attribute__((aligned(16))) float sm_o[kWaves][G][HD];
+  __shared__ float sm_m[kWaves][NC];   // each wave's reference max
+  __shared__ float sm_t[kWaves][NC];   // each wave's exact max
+  __shared__ float sm_s[kWaves][NC];
+  __shared__ __attribute__((aligned(16))) float sm_o[kWaves][NC][HD];
 
   // a1 + a2: live length and this split's rows; with several query rows,
-  // this row's rows end at min(hi, its own live length).
+  // a row's rows end at min(hi, its own live length). The waves run to the
+  // end of the workgroup's last row; masking starts at its first row's end,
+  // and each column stops at its own row's end.
   const detail::SplitRange rg = detail::split_range(a, sp, b);
   const long long lo = rg.lo;
-  const long long hi = detail::row_end(a, rs, rg.hi);
+  const int gq = col & 7;                            // this lane's column
+  long long hi, mask_from, col_end;
+  bool col_valid;                                    // column maps to a row
+  int col_t, col_g;                                  // and its (row, head)
+  if constexpr (R == 1) {
+    hi = detail::row_end(a, rs, rg.hi);
+    mask_from = hi;
+    col_end = hi;
+    col_valid = gq < G;
+    col_t = rs.t;
+    col_g = gq < G ? gq : 0;
+  } else {
+    const int t_last = min(rs.t + R - 1, a.n_q - 1);
+    hi = detail::row_end_at(a, b, t_last, rg.hi);
+    mask_from = detail::row_end_at(a, b, rs.t, rg.hi);
+    const int r_c = gq / G;
+    col_valid = gq < NC && rs.t + r_c < a.n_q;
+    col_t = col_valid ? rs.t + r_c : rs.t;
+    col_g = col_valid ? gq - r_c * G : 0;
+    col_end = col_valid ? detail::row_end_at(a, b, col_t, rg.hi) : hi;
+  }
 
   // This (sequence, KV head) slice of the caches: row r at byte r * row_bytes.
   const uint32_t row_bytes = (uint32_t)(a.n_kv_head * HD * 2);
@@ -347,6 +388,8 @@ partial_mfma_kernel(PartialArgs a) {
   const LaneOffsets lo_off = lane_offsets<HD>(row_bytes, col, grp, lane);
   unsigned char *vlds = sm_v + wave * Geo::VTILE;
   const uint32_t hi32 = (uint32_t)hi;
+  const uint32_t mask32 = (uint32_t)mask_from;
+  const uint32_t lim32 = (uint32_t)col_end;
   const uint32_t step = (uint32_t)(kWaves * kTileRows);
   uint32_t t0 = (uint32_t)lo + (uint32_t)(wave * kTileRows);
   if (lo >= hi) t0 = hi32;  // idle split
@@ -372,15 +415,14 @@ partial_mfma_kernel(PartialArgs a) {
     TileRegs<HD> ta, tb;
     load_tile<HD>(ta, kseq, vseq, row_bytes, t0, hi32, lo_off);
 
-    // a3: B operand of S = K·Q'ᵀ: column col holds head (col % 8), hi part in
-    // columns 0..7 and lo part in 8..15 (zero for heads past G), dims
-    // 32*ks + 8*grp + e, pre-scaled to base-2 units.
-    const int gq = col & 7;
+    // a3: B operand of S = K·Q'ᵀ: column col holds (row, head) col % 8, hi
+    // part in columns 0..7 and lo part in 8..15 (zero for unused columns),
+    // dims 32*ks + 8*grp + e, pre-scaled to base-2 units.
     float4 qraw[Geo::KS][2];
     {
+      const detail::RowSel qs{b, col_t};
       const float *qrow =
-          a.q + detail::q_offset(a, rs, hy * G + (gq < G ? gq : 0), HD) +
-          8 * grp;
+          a.q + detail::q_offset(a, qs, hy * G + col_g, HD) + 8 * grp;
 #pragma unroll
       for (int ks = 0; ks < Geo::KS; ++ks) {
         qraw[ks][0] = *reinterpret_cast<const float4 *>(qrow + 32 * ks);
@@ -403,7 +445,7 @@ partial_mfma_kernel(PartialArgs a) {
         const _Float16 h = (_Float16)(x[e] * a.scale_log2);
         const float lo = __builtin_fmaf(x[e], a.scale_log2, -(float)h);
         const _Float16 val = hi_col ? h : (_Float16)lo;
-        qf[ks][e] = (gq < G) ? val : (_Float16)0.0f;
+        qf[ks][e] = col_valid ? val : (_Float16)0.0f;
       }
     }
 
@@ -416,7 +458,7 @@ partial_mfma_kernel(PartialArgs a) {
       // invariant: ta holds tile t0, tb holds tile t0 + step
       while (true) {
         const uint32_t t1 = t0 + step;
-        compute_tile<HD>(ta, t0, hi32, qf, oacc, m_run, m_true, s_run, vlds, col, grp,
+        compute_tile<HD, (R > 1)>(ta, t0, mask32, lim32, qf, oacc, m_run, m_true, s_run, vlds, col, grp,
                          lane, hi_col);
         if (t1 >= hi32) break;
         // Inside the loop the next tile is loaded only if it has rows: even
@@ -424,7 +466,7 @@ partial_mfma_kernel(PartialArgs a) {
         // a few tiles.
         if (t1 + step < hi32)
           load_tile<HD>(ta, kseq, vseq, row_bytes, t1 + step, hi32, lo_off);
-        compute_tile<HD>(tb, t1, hi32, qf, oacc, m_run, m_true, s_run, vlds, col, grp,
+        compute_tile<HD, (R > 1)>(tb, t1, mask32, lim32, qf, oacc, m_run, m_true, s_run, vlds, col, grp,
                          lane, hi_col);
         t0 = t1 + step;
         if (t0 >= hi32) break;
@@ -433,7 +475,7 @@ partial_mfma_kernel(PartialArgs a) {
       }
     } else {
       while (true) {
-        compute_tile<HD>(ta, t0, hi32, qf, oacc, m_run, m_true, s_run, vlds, col, grp,
+        compute_tile<HD, (R > 1)>(ta, t0, mask32, lim32, qf, oacc, m_run, m_true, s_run, vlds, col, grp,
                          lane, hi_col);
         t0 += step;
         if (t0 >= hi32) break;
@@ -448,7 +490,7 @@ partial_mfma_kernel(PartialArgs a) {
   // one head's output over the four waves with weights exp2(m_ref - m_all),
   // m_all the largest exact max: the record is relative to the exact max.
   s_run = pair32_sum(pair16_sum(s_run));
-  if (grp == 0 && col < G) {
+  if (grp == 0 && col < NC) {
     sm_m[wave][col] = m_run;
     sm_t[wave][col] = m_true;
     sm_s[wave][col] = s_run;
@@ -458,7 +500,7 @@ partial_mfma_kernel(PartialArgs a) {
     float o4[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) o4[r] = add_ror8(oacc[i][r]);
-    if (col < G)
+    if (col < NC)
       *reinterpret_cast<float4 *>(&sm_o[wave][col][16 * i + 4 * grp]) =
           make_float4(o4[0], o4[1], o4[2], o4[3]);
   }
@@ -466,9 +508,12 @@ partial_mfma_kernel(PartialArgs a) {
   constexpr int D4 = HD / 4;
   const size_t pstr = 4 + HD;
   float *rec0 = a.partials + detail::rec_offset(a, rs, sp, hy * G, HD);
-  for (int idx = tid; idx < G * D4; idx += kThreads) {
+  for (int idx = tid; idx < NC * D4; idx += kThreads) {
     const int gg = idx / D4;
     const int d4 = idx % D4;
+    // column gg = (row r, head g); rows past n_q have no record
+    const int r = gg / G;
+    if (R > 1 && rs.t + r >= a.n_q) continue;
     float mm = neg_inf();
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, sm_t[w][gg]);
@@ -485,7 +530,8 @@ partial_mfma_kernel(PartialArgs a) {
       acc.w = fmaf(c, x.w, acc.w);
       st = fmaf(c, sm_s[w][gg], st);
     }
-    float *rec = rec0 + (size_t)gg * pstr;
+    float *rec = rec0 + (size_t)(gg - r * G) * pstr +
+                 (size_t)r * a.n_head * pstr;  // row t + r: n_head records on
     *reinterpret_cast<float4 *>(rec + 4 + 4 * d4) = acc;
     if (d4 == 0)
       *reinterpret_cast<float4 *>(rec) = make_float4(
@@ -518,6 +564,41 @@ hipError_t launch_hd(int group, const PartialArgs &a, int batch,
   }
 }
 
+// Query rows per workgroup for n_q rows at group size G: as many as the 8
+// MFMA columns hold (G * R <= 8, R in {1, 2, 4, 8}), and no more than the
+// smallest such R that covers n_q.
+int rows_per_workgroup(int group, int n_q) {
+  if (n_q <= 1) return 1;
+  const int cap = group == 1 ? 8 : group == 2 ? 4 : group <= 4 ? 2 : 1;
+  int r = 1;
+  while (r < cap && r < n_q) r *= 2;
+  return r;
+}
+
+template <int HD, int G, int R>
+hipError_t launch_rows(const PartialArgs &a, int batch, hipStream_t stream) {
+  const int nrb = (a.n_q + R - 1) / R;
+  hipLaunchKernelGGL((partial_mfma_kernel<HD, G, false, R>),
+                     dim3(a.n_splits, a.n_kv_head, batch * nrb),
+                     dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int HD>
+hipError_t launch_rows_hd(int group, int rows, const PartialArgs &a,
+                          int batch, hipStream_t stream) {
+  switch (group * 16 + rows) {
+    case 1 * 16 + 2: return launch_rows<HD, 1, 2>(a, batch, stream);
+    case 1 * 16 + 4: return launch_rows<HD, 1, 4>(a, batch, stream);
+    case 1 * 16 + 8: return launch_rows<HD, 1, 8>(a, batch, stream);
+    case 2 * 16 + 2: return launch_rows<HD, 2, 2>(a, batch, stream);
+    case 2 * 16 + 4: return launch_rows<HD, 2, 4>(a, batch, stream);
+    case 3 * 16 + 2: return launch_rows<HD, 3, 2>(a, batch, stream);
+    case 4 * 16 + 2: return launch_rows<HD, 4, 2>(a, batch, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 template <int HD>
 hipError_t launch_per_head(const PartialArgs &a, int batch, hipStream_t stream) {
   hipLaunchKernelGGL((partial_mfma_kernel<HD, 1, true>),
@@ -540,6 +621,15 @@ hipError_t launch_partial_per_head(int head_dim, const PartialArgs &a,
 
 hipError_t launch_partial_mfma(int head_dim, int group, const PartialArgs &a,
                                int batch, hipStream_t stream) {
+  const int rows = rows_per_workgroup(group, a.n_q);
+  if (rows > 1) {
+    switch (head_dim) {
+      case 64: return launch_rows_hd<64>(group, rows, a, batch, stream);
+      case 128: return launch_rows_hd<128>(group, rows, a, batch, stream);
+      case 256: return launch_rows_hd<256>(group, rows, a, batch, stream);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (head_dim) {
     case 64: return launch_hd<64>(group, a, batch, stream);
     case 128: return launch_hd<128>(group, a, batch, stream);

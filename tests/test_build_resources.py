@@ -39,9 +39,12 @@ def test_every_kernel_without_scratch_or_spills():
     ks = _kernels(_report())
     partial = [k for k in ks if "partial_" in k]
     per_head = [k for k in partial if "ELb1E" in k]
+    rows = [k for k in partial if re.search(r"ELb0ELi[248]E", k)]
     # 6 head dims x 8 group sizes, the 3 per-query-head forms (hd 64/128/256),
-    # plus combine, append and probe kernels
-    assert len(partial) == 51 and len(per_head) == 3, (len(partial), per_head)
+    # 7 (group, rows) forms for several query rows x 3 head dims, plus
+    # combine, append and probe kernels
+    assert len(partial) == 72 and len(per_head) == 3 and len(rows) == 21, \
+        (len(partial), len(per_head), len(rows))
     assert any("combine_kernel" in k for k in ks)
     for name, f in ks.items():
         assert f.get("ScratchSize", 0) == 0, (name, f)
@@ -67,11 +70,17 @@ def test_workgroups_per_cu_matches_compiler_report(splitkv_lib_path):
     seen = 0
     for name, f in ks.items():
         m = re.search(r"partial_(?:mfma|valu)_kernelILi(\d+)ELi(\d+)E", name)
-        if not m or "ELb1E" in name:      # the per-query-head form aside
-            continue
+        if not m or "ELb1E" in name or re.search(r"ELb0ELi[248]E", name):
+            continue                  # the per-head and several-row forms aside
         hd, g = int(m.group(1)), int(m.group(2))
         assert skv.workgroups_per_cu(hd, g) == f["Occupancy"], (hd, g, f)
         seen += 1
     assert seen == 48
+    # the several-row forms fit as many workgroups per CU as the one-row form
+    for name, f in ks.items():
+        m = re.search(r"partial_mfma_kernelILi(\d+)ELi(\d+)ELb0ELi[248]E", name)
+        if m:
+            hd, g = int(m.group(1)), int(m.group(2))
+            assert skv.workgroups_per_cu(hd, g) == f["Occupancy"], (name, f)
     assert skv.workgroups_per_cu(96, 4) == 0
     assert skv.workgroups_per_cu(128, 9) == 0
