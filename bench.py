@@ -18,6 +18,9 @@ Reported (one JSON line on stdout):
               rocprofv3 counters (profiles/), or null when the counters were
               taken on another version of the kernel source
   cpu_baseline  the fp64 oracle on the host, one core, on one layer
+  also        pct_of_probe (against the read stream measured on this GPU),
+              total_bytes_per_layer / total_gbps (q, K+V, records written
+              and read back, output)
 
 Usage: python bench.py [--steps K] [--warmup W] [--nkv N] [--layers L]
        python bench.py --sweep          # split-count sweep, one line per point
@@ -332,6 +335,10 @@ def run_main(args):
     probe = hbm_read_probe(torch, skv) if not args.no_probe else None
 
     cpu = cpu_baseline(lay, args.nkv, args.cpu_budget) if not args.no_cpu else None
+    # every byte a layer moves: q, K+V, the records written by the partial
+    # kernel and read back by the combine, and the output
+    rec_bytes = skv.partials_bytes(1, 28, 128, S)
+    total_layer = 28 * 128 * 4 + kv_layer + 2 * rec_bytes + 28 * 128 * 4
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -364,6 +371,9 @@ def run_main(args):
                      "traffic_source": traffic_src},
         "combine_avg_launch_us": round(c_mean * 1e3, 3),
         "hbm_read_probe_gbps": round(probe, 1) if probe else None,
+        "pct_of_probe": round(100 * value / probe, 2) if probe else None,
+        "total_bytes_per_layer": total_layer,
+        "total_gbps": round(total_layer * args.layers / (ms_step * 1e-3) / 1e9, 1),
         "points": points,
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 4),
