@@ -756,9 +756,11 @@ def run_sweep(args):
     import synth
     max_ctx = synth.CFG3.max_ctx
     cu = torch.cuda.get_device_properties(0).multi_processor_count
+    case = None
     for S, blk in [(s, 0) for s in args.sweep_splits] + \
                   [(-(-max_ctx // b), b) for b in args.sweep_blocks]:
-        lay = Layers(args.layers, max_ctx, S, blk)
+        lay = Layers(args.layers, max_ctx, S, blk, case=case)
+        case = lay.case
         graph = lay.capture()
         for nkv in args.points:
             lay.set_nkv(nkv)

@@ -153,9 +153,9 @@ int splitkv_workgroups_per_cu(int head_dim, int group) {
     case 8: { static const int t[8] = {4, 4, 3, 3, 2, 2, 2, 2}; return t[group - 1]; }
     case 16: { static const int t[8] = {4, 3, 3, 2, 2, 2, 2, 1}; return t[group - 1]; }
     case 32: { static const int t[8] = {4, 3, 3, 2, 2, 2, 2, 1}; return t[group - 1]; }
-    case 64: return 4;
-    case 128: return 2;
-    case 256: return 1;
+    case 64: return 5;
+    case 128: return 3;
+    case 256: return 2;
     default: return 0;
   }
 }
@@ -169,7 +169,13 @@ int splitkv_pick_splits(int batch, int n_head, int n_kv_head, int head_dim,
   if (st != SPLITKV_OK) return st;
   const int group = n_head / n_kv_head;
   const long long units = (long long)batch * n_kv_head;
-  const long long wpc = splitkv_workgroups_per_cu(head_dim, group);
+  long long wpc = splitkv_workgroups_per_cu(head_dim, group);
+  // The matrix-core kernel (head_dim >= 64) keeps two 16-row K/V tiles in
+  // flight per wave, 4 waves x 2 x 16 x 4*head_dim bytes per workgroup: at
+  // 256 / head_dim workgroups per compute unit that is 128 KB in flight per
+  // compute unit, enough to cover the memory latency; more resident
+  // workgroups only add per-split fixed costs (query load, merge, records).
+  if (head_dim >= 64 && wpc > 256 / head_dim) wpc = 256 / head_dim;
   // One full round of resident workgroups. With one sequence every split
   // has the same work, so a single round is best; a few workgroups past it
   // would cost a whole second round, hence the floor.

@@ -16,7 +16,9 @@
 // vector FMAs these cost 2*G*hd FMAs per row plus the dot-product
 // reductions, which measured at about 78 wave instructions per KV row for
 // 28q/4kv hd128 (the VALU issue limit lands near half of the HBM rate). On
-// v_mfma_f32_16x16x32_f16 they take two MFMAs per 16 rows and 16 dims.
+// the matrix cores they take one v_mfma_f32_16x16x32_f16 per 16 rows and 32
+// dims (scores) and one v_mfma_f32_16x16x16_f16 per 16 rows and 16 dims
+// (output).
 //
 // Precision: the MFMA takes fp16 operands and accumulates in fp32. K and V
 // are fp16 already. q (scaled by scale*log2(e)) and the softmax weights p are
@@ -25,18 +27,29 @@
 // heads' hi parts in columns 0..7 and their lo parts in columns 8..15, so one
 // MFMA computes both halves and a DPP row rotation by 8 adds them.
 //
-// Data flow of one wave over a tile of 32 rows (a workgroup's waves take
+// Data flow of one wave over a tile of 16 rows (a workgroup's waves take
 // interleaved tiles; the next tile's loads are issued before the current tile
-// is computed):
-//   K: lane l loads 16 bytes of row (l % 16) at dims 32*ks + 8*(l/16): the
-//      A operand of S = K·Q'ᵀ directly (fp16, 16-byte coalesced loads);
+// is computed, so two tiles per wave are in flight):
+//   K, V: 16-byte loads that each cover whole 256-byte rows (one instruction
+//      = 64 lanes = 4 rows of hd 128), so every cache line a load touches is
+//      used in full. A load pattern shaped like the MFMA operand (16 rows x
+//      64 bytes per instruction, two instructions per line) measured ~1.2 us
+//      slower per 64 MB launch;
+//   K: written row-major into the wave's LDS slice (rows 16 bytes past a
+//      multiple of 256, so the 16 rows of an operand read hit 16 different
+//      bank groups) and read back as the A operand of S = K·Q'ᵀ: lane l holds
+//      row l % 16, dims 32*ks + 8*(l/16);
 //   scores: D lane l holds rows 4*(l/16)+r of its column l % 16 -> max over
-//      the tile by in-lane max and two cross-group shuffles, p = exp2(s - m);
-//   p: already in the B-operand layout of O += Vᵀ·P (8 rows per lane);
-//   V: 16-byte coalesced loads, written row-major into the wave's LDS slice
-//      (rows padded by 32 bytes against bank conflicts), read back with the
-//      gfx950 transposing LDS read (ds_read_b64_tr_b16), which delivers four
-//      rows of one dim per lane: the A operand of Vᵀ·P.
+//      the tile by in-lane max and two cross-group exchanges,
+//      p = exp2(s - m);
+//   p: already in the B-operand layout of O += Vᵀ·P (4 rows per lane);
+//   V: written row-major into the wave's LDS slice (rows padded by 32 bytes
+//      against bank conflicts), read back with the gfx950 transposing LDS
+//      read (ds_read_b64_tr_b16), which delivers four rows of one dim per
+//      lane: the A operand of Vᵀ·P on v_mfma_f32_16x16x16_f16.
+// The kernel template also builds 32- and 64-row tiles (k = 32 MFMA for the
+// output) and the operand-shaped K loads for A/B measurements; the launched
+// form is 16 rows with K through LDS.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -58,27 +71,32 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 typedef short short4v __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) short4v lds_short4v;
 
-constexpr int kTileRows = 32;
 constexpr int kRor8 = 0x128;  // DPP row_ror:8 (rotate by 8 within 16 lanes)
 constexpr float kLazyLog2 = 8.0f;  // reference-max lag allowed (base-2 units)
 
-template <int HD>
+template <int HD, int TR>
 struct MGeo {
   static constexpr int KS = HD / 32;               // q·k k-steps of 32 dims
   static constexpr int DB = HD / 16;               // p·v output blocks of 16 dims
   static constexpr int LPR = HD / 8;               // lanes per row (V staging)
   static constexpr int RPI = 64 / LPR;             // rows per staging load
-  static constexpr int NV = kTileRows / RPI;       // staging loads per tile
+  static constexpr int RG = TR / 16;               // 16-row groups per tile
+  static constexpr int NV = TR / RPI;              // staging loads per tile
   static constexpr int VSTR = HD * 2 + 32;         // LDS bytes per staged row
-  static constexpr int VTILE = kTileRows * VSTR;   // LDS bytes per wave
-  static constexpr bool kPrefetch = HD <= 128;     // two tiles in registers
+  static constexpr int VR = TR < 32 ? TR : 32;     // rows staged at a time
+  static constexpr int VTILE = VR * VSTR;          // LDS bytes of staged V
+  static constexpr int KSTR = HD * 2 + 16;         // LDS bytes per staged K row
+  static constexpr int KTILE = TR * KSTR;          // LDS bytes of staged K
+  // two tiles in registers when a tile holds at most 64 VGPRs of K/V
+  static constexpr bool kPrefetch = HD * TR <= 128 * 32;
   static_assert(HD % 32 == 0 && HD <= 256, "head_dim");
+  static_assert(TR == 16 || TR == 32 || TR == 64, "tile rows");
 };
 
-template <int HD>
+template <int HD, int TR>
 struct TileRegs {
-  uint4 k[2][MGeo<HD>::KS];
-  uint4 v[MGeo<HD>::NV];
+  uint4 k[MGeo<HD, TR>::RG][MGeo<HD, TR>::KS];
+  uint4 v[MGeo<HD, TR>::NV];
 };
 
 __device__ __forceinline__ half8 as_half8(const uint4 &u) {
@@ -156,7 +174,7 @@ template <int HD>
 __device__ __forceinline__ LaneOffsets lane_offsets(uint32_t row_bytes,
                                                     int col, int grp,
                                                     int lane) {
-  using Geo = MGeo<HD>;
+  using Geo = MGeo<HD, 16>;
   LaneOffsets o;
   o.k = (uint32_t)col * row_bytes + 16u * grp;
   o.v = (uint32_t)(lane / Geo::LPR) * row_bytes +
@@ -176,18 +194,29 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_view(
       limit, kBufferWord3);
 }
 
-// Issue the loads of the 32-row tile starting at row tb (tb < hi).
-template <int HD>
-__device__ __forceinline__ void load_tile(TileRegs<HD> &t, const uint16_t *kseq,
+// Issue the loads of the TR-row tile starting at row tb (tb < hi).
+template <int HD, int TR, bool KL>
+__device__ __forceinline__ void load_tile(TileRegs<HD, TR> &t,
+                                          const uint16_t *kseq,
                                           const uint16_t *vseq,
                                           uint32_t row_bytes, uint32_t tb,
                                           uint32_t hi, const LaneOffsets &o) {
-  using Geo = MGeo<HD>;
+  using Geo = MGeo<HD, TR>;
+  if constexpr (KL) {
+    // whole rows, as for V: instruction i covers rows RPI*i .. RPI*i + RPI-1
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
-    const __amdgpu_buffer_rsrc_t r = rows_view(kseq, row_bytes, tb + 16u * rt, hi);
+    for (int i = 0; i < Geo::RG * Geo::KS; ++i) {
+      const __amdgpu_buffer_rsrc_t r =
+          rows_view(kseq, row_bytes, tb + (uint32_t)(Geo::RPI * i), hi);
+      t.k[i / Geo::KS][i % Geo::KS] = load16(r, o.v);
+    }
+  } else {
 #pragma unroll
-    for (int ks = 0; ks < Geo::KS; ++ks) t.k[rt][ks] = load16(r, o.k + 64u * ks);
+    for (int rt = 0; rt < Geo::RG; ++rt) {
+      const __amdgpu_buffer_rsrc_t r = rows_view(kseq, row_bytes, tb + 16u * rt, hi);
+#pragma unroll
+      for (int ks = 0; ks < Geo::KS; ++ks) t.k[rt][ks] = load16(r, o.k + 64u * ks);
+    }
   }
 #pragma unroll
   for (int i = 0; i < Geo::NV; ++i) {
@@ -201,35 +230,62 @@ __device__ __forceinline__ void load_tile(TileRegs<HD> &t, const uint16_t *kseq,
 // lane's column's end row (equal to mask_from with one query row per
 // workgroup). SAFE: a column may have no live row yet (several query rows per
 // workgroup), so -inf maxima are guarded.
-template <int HD, bool SAFE>
+template <int HD, int TR, bool KL, bool SAFE>
 __device__ __forceinline__ void compute_tile(
-    const TileRegs<HD> &t, uint32_t tb, uint32_t mask_from, uint32_t lim,
-    const half8 (&qf)[MGeo<HD>::KS], float4v (&oacc)[MGeo<HD>::DB],
-    float &m_run, float &m_true, float &s_run, unsigned char *vlds, int col,
-    int grp,
-    int lane, bool hi_col) {
-  using Geo = MGeo<HD>;
-  // a4: scores S = K · Q'ᵀ for the tile's two 16-row groups.
-  float4v sc[2];
+    const TileRegs<HD, TR> &t, uint32_t tb, uint32_t mask_from, uint32_t lim,
+    const half8 (&qf)[MGeo<HD, TR>::KS], float4v (&oacc)[MGeo<HD, TR>::DB],
+    float &m_run, float &m_true, float &s_run, unsigned char *slice, int col,
+    int grp, int lane, bool hi_col) {
+  using Geo = MGeo<HD, TR>;
+  constexpr int RG = Geo::RG;
+  unsigned char *vlds = slice + (KL ? Geo::KTILE : 0);
+  // K operands: straight from the loads, or (KL) whole rows through LDS:
+  // written row-major with KSTR-byte rows, read back as lane l = row l % 16,
+  // dims 32*ks + 8*(l/16) (row pitch 16 bytes past a multiple of 256: the 16
+  // rows of a read fall in 16 different bank groups).
+  uint4 ka[RG][Geo::KS];
+  if constexpr (KL) {
+    wave_lds_fence();
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
+    for (int i = 0; i < RG * Geo::KS; ++i) {
+      const int rl = Geo::RPI * i + lane / Geo::LPR;
+      *reinterpret_cast<uint4 *>(slice + rl * Geo::KSTR +
+                                 16 * (lane % Geo::LPR)) = t.k[i / Geo::KS][i % Geo::KS];
+    }
+    wave_lds_fence();
+#pragma unroll
+    for (int rt = 0; rt < RG; ++rt)
+#pragma unroll
+      for (int ks = 0; ks < Geo::KS; ++ks)
+        ka[rt][ks] = *reinterpret_cast<const uint4 *>(
+            slice + (16 * rt + col) * Geo::KSTR + 64 * ks + 16 * grp);
+  } else {
+#pragma unroll
+    for (int rt = 0; rt < RG; ++rt)
+#pragma unroll
+      for (int ks = 0; ks < Geo::KS; ++ks) ka[rt][ks] = t.k[rt][ks];
+  }
+  // a4: scores S = K · Q'ᵀ for the tile's 16-row groups.
+  float4v sc[RG];
+#pragma unroll
+  for (int rt = 0; rt < RG; ++rt) {
     sc[rt] = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < Geo::KS; ++ks)
-      sc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(t.k[rt][ks]),
+      sc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(ka[rt][ks]),
                                                       qf[ks], sc[rt], 0, 0, 0);
   }
   // hi + lo columns; rows at or past the column's end (last tiles only) score
   // -inf.
-  float s[2][4];
+  float s[RG][4];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
+  for (int rt = 0; rt < RG; ++rt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) s[rt][r] = add_ror8(sc[rt][r]);
   }
-  if (tb + kTileRows > mask_from) {
+  if (tb + TR > mask_from) {
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt) {
+    for (int rt = 0; rt < RG; ++rt) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (tb + (uint32_t)(16 * rt + 4 * grp + r) >= lim) s[rt][r] = neg_inf();
@@ -237,7 +293,7 @@ __device__ __forceinline__ void compute_tile(
   }
   float mt = neg_inf();
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
+  for (int rt = 0; rt < RG; ++rt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) mt = fmaxf(mt, s[rt][r]);
   }
@@ -255,10 +311,11 @@ __device__ __forceinline__ void compute_tile(
   // 0 while m_run is -inf (and with SAFE also while mn still is)
   const float corr = (SAFE && m_run == neg_inf()) ? 0.0f : fast_exp2(m_run - mn);
   const float mref = (SAFE && mn == neg_inf()) ? 0.0f : mn;
-  half8 pf;
-  float pv[8];
+  // p hi or lo parts in this lane's rows: the B operand of O += Vᵀ·P
+  _Float16 pf[4 * RG];
+  float pv[4 * RG];
 #pragma unroll
-  for (int rt = 0; rt < 2; ++rt) {
+  for (int rt = 0; rt < RG; ++rt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const float p = fast_exp2(s[rt][r] - mref);  // exp2(-inf) = 0
@@ -267,9 +324,14 @@ __device__ __forceinline__ void compute_tile(
       pf[4 * rt + r] = hi_col ? h : (_Float16)(p - (float)h);
     }
   }
-  // the tile's weight sum as a tree (no 8-long dependent chain)
-  const float psum = ((pv[0] + pv[1]) + (pv[2] + pv[3])) +
-                     ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+  // the tile's weight sum as a tree (no long dependent chain)
+  float psum4[RG];
+#pragma unroll
+  for (int rt = 0; rt < RG; ++rt)
+    psum4[rt] = (pv[4 * rt] + pv[4 * rt + 1]) + (pv[4 * rt + 2] + pv[4 * rt + 3]);
+  float psum = psum4[0];
+  if constexpr (RG == 2) psum = psum4[0] + psum4[1];
+  if constexpr (RG == 4) psum = (psum4[0] + psum4[1]) + (psum4[2] + psum4[3]);
   // Rescale only when some column's reference moved (else corr is 1 for
   // every column and the products would change nothing).
   if (__any(mn != m_run)) {
@@ -280,33 +342,50 @@ __device__ __forceinline__ void compute_tile(
   s_run += psum;
   m_run = mn;
 
-  // V tile into this wave's LDS slice, row-major with padded rows.
-  wave_lds_fence();
-#pragma unroll
-  for (int i = 0; i < Geo::NV; ++i) {
-    const int rl = Geo::RPI * i + lane / Geo::LPR;
-    *reinterpret_cast<uint4 *>(vlds + rl * Geo::VSTR +
-                               16 * (lane % Geo::LPR)) = t.v[i];
-  }
-  wave_lds_fence();
-  // O += Vᵀ · P: lane (grp, col) reads dim 16b + col of rows 4*grp + 0..3
-  // and 16 + 4*grp + 0..3 (the same row order as its 8 p values).
+  // O += Vᵀ · P, 32 rows (16 with one row group) at a time: the V rows go
+  // into this wave's LDS slice, row-major with padded rows, and lane
+  // (grp, col) reads back dim 16b + col of rows 4*grp + 0..3 and
+  // 16 + 4*grp + 0..3, the same row order as its p values. One row group:
+  // the k = 16 MFMA; otherwise the k = 32 MFMA per 32 rows.
   const int c4 = col >> 2;
   const int cm = col & 3;
+  constexpr int NH = RG >= 2 ? RG / 2 : 1;    // 32-row halves
+  constexpr int NVH = Geo::NV / NH;           // staging loads per half
 #pragma unroll
-  for (int b = 0; b < Geo::DB; ++b) {
-    const int byte_col = (16 * b + 4 * cm) * 2;
-    // address-space conversion of the generic LDS pointer (C-style cast)
-    lds_short4v *a0 =
-        (lds_short4v *)(vlds + (4 * grp + c4) * Geo::VSTR + byte_col);
-    lds_short4v *a1 =
-        (lds_short4v *)(vlds + (16 + 4 * grp + c4) * Geo::VSTR + byte_col);
-    const short4v r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(a0);
-    const short4v r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(a1);
-    const half8 vf = __builtin_shufflevector(__builtin_bit_cast(half4, r0),
-                                             __builtin_bit_cast(half4, r1), 0,
-                                             1, 2, 3, 4, 5, 6, 7);
-    oacc[b] = __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pf, oacc[b], 0, 0, 0);
+  for (int h = 0; h < NH; ++h) {
+    wave_lds_fence();
+#pragma unroll
+    for (int i = 0; i < NVH; ++i) {
+      const int rl = Geo::RPI * i + lane / Geo::LPR;
+      *reinterpret_cast<uint4 *>(vlds + rl * Geo::VSTR +
+                                 16 * (lane % Geo::LPR)) = t.v[NVH * h + i];
+    }
+    wave_lds_fence();
+#pragma unroll
+    for (int b = 0; b < Geo::DB; ++b) {
+      const int byte_col = (16 * b + 4 * cm) * 2;
+      // (C-style casts: address-space conversion of the generic LDS pointer)
+      lds_short4v *a0 =
+          (lds_short4v *)(vlds + (4 * grp + c4) * Geo::VSTR + byte_col);
+      const short4v r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(a0);
+      if constexpr (RG >= 2) {
+        lds_short4v *a1 =
+            (lds_short4v *)(vlds + (16 + 4 * grp + c4) * Geo::VSTR + byte_col);
+        const short4v r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(a1);
+        const half8 vf = __builtin_shufflevector(__builtin_bit_cast(half4, r0),
+                                                 __builtin_bit_cast(half4, r1),
+                                                 0, 1, 2, 3, 4, 5, 6, 7);
+        const half8 pb = {pf[8 * h], pf[8 * h + 1], pf[8 * h + 2],
+                          pf[8 * h + 3], pf[8 * h + 4], pf[8 * h + 5],
+                          pf[8 * h + 6], pf[8 * h + 7]};
+        oacc[b] =
+            __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pb, oacc[b], 0, 0, 0);
+      } else {
+        const half4 pb = {pf[0], pf[1], pf[2], pf[3]};
+        oacc[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+            __builtin_bit_cast(half4, r0), pb, oacc[b], 0, 0, 0);
+      }
+    }
   }
 }
 
@@ -318,10 +397,14 @@ __device__ __forceinline__ void compute_tile(
 // R: query rows per workgroup (several query rows per sequence). The MFMA
 // columns then hold (row, head) pairs, column c = r * G + g, so every K/V row
 // is read once for the R rows; with R = 1 each workgroup serves one row.
-template <int HD, int G, bool PER_HEAD = false, int R = 1>
-__global__ __launch_bounds__(kThreads, HD >= 256 ? 1 : 2) void
+template <int HD, int G, bool PER_HEAD = false, int R = 1, int TR = 16,
+          bool KL = true>
+__global__ __launch_bounds__(kThreads, 2) void
 partial_mfma_kernel(PartialArgs a) {
-  using Geo = MGeo<HD>;
+  using Geo = MGeo<HD, TR>;
+  // LDS per wave: staged K (KL) and V; after the last tile the same bytes
+  // hold the wave's unnormalised output for the workgroup merge.
+  constexpr int SLICE = (KL ? Geo::KTILE : 0) + Geo::VTILE;
   constexpr int NC = G * R;                          // MFMA columns in use
   static_assert(G >= 1 && G <= 8 && NC <= 8, "group x rows");
   static_assert(!PER_HEAD || (G == 1 && R == 1), "per-head form: one head");
@@ -346,11 +429,11 @@ partial_mfma_kernel(PartialArgs a) {
   const int grp = lane >> 4;
   const bool hi_col = col < 8;
 
-  __shared__ __attribute__((aligned(16))) unsigned char sm_v[kWaves * Geo::VTILE];
+  __shared__ __attribute__((aligned(16))) unsigned char sm_v[kWaves * SLICE];
   __shared__ float sm_m[kWaves][NC];   // each wave's reference max
   __shared__ float sm_t[kWaves][NC];   // each wave's exact max
   __shared__ float sm_s[kWaves][NC];
-  __shared__ __attribute__((aligned(16))) float sm_o[kWaves][NC][HD];
+  static_assert(NC * HD * 4 <= SLICE, "output state fits the wave's slice");
 
   // a1 + a2: live length and this split's rows; with several query rows,
   // a row's rows end at min(hi, its own live length). The waves run to the
@@ -386,12 +469,12 @@ partial_mfma_kernel(PartialArgs a) {
   const uint16_t *kseq = a.k + seq_base;
   const uint16_t *vseq = a.v + seq_base;
   const LaneOffsets lo_off = lane_offsets<HD>(row_bytes, col, grp, lane);
-  unsigned char *vlds = sm_v + wave * Geo::VTILE;
+  unsigned char *vlds = sm_v + wave * SLICE;
   const uint32_t hi32 = (uint32_t)hi;
   const uint32_t mask32 = (uint32_t)mask_from;
   const uint32_t lim32 = (uint32_t)col_end;
-  const uint32_t step = (uint32_t)(kWaves * kTileRows);
-  uint32_t t0 = (uint32_t)lo + (uint32_t)(wave * kTileRows);
+  const uint32_t step = (uint32_t)(kWaves * TR);
+  uint32_t t0 = (uint32_t)lo + (uint32_t)(wave * TR);
   if (lo >= hi) t0 = hi32;  // idle split
 
   float4v oacc[Geo::DB];
@@ -404,17 +487,13 @@ partial_mfma_kernel(PartialArgs a) {
   // A wave whose first tile starts at or past hi has no rows: it keeps the
   // empty state (-inf, 0, 0) and issues no loads at all.
   if (t0 < hi32) {
-    // Issue order: first tile's K/V, then the queries, then the second tile.
-    // The first K/V requests must not wait behind the query conversion, whose
-    // loads queue behind the other waves' streaming traffic; converting the
-    // queries waits only for the loads issued before them. The second tile's
-    // loads are issued unconditionally: a tile at or past hi has a zero record
-    // limit, so its loads return zeros without touching memory, and the wait
-    // before the query conversion stays exact (a conditional load between
-    // the query loads and their use makes the compiler wait for it too).
-    TileRegs<HD> ta, tb;
-    load_tile<HD>(ta, kseq, vseq, row_bytes, t0, hi32, lo_off);
-
+    // Issue order: the queries, the first tile's K/V, the query conversion
+    // (it waits for the query loads only, which come back while the tile is
+    // in flight), then the second tile. Delaying the second tile by the
+    // conversion lets the first tiles of all resident waves reach the memory
+    // queues ahead of any second tile, so first tiles land early and their
+    // compute overlaps the rest of the stream.
+    //
     // a3: B operand of S = K·Q'ᵀ: column col holds (row, head) col % 8, hi
     // part in columns 0..7 and lo part in 8..15 (zero for unused columns),
     // dims 32*ks + 8*grp + e, pre-scaled to base-2 units.
@@ -429,8 +508,8 @@ partial_mfma_kernel(PartialArgs a) {
         qraw[ks][1] = *reinterpret_cast<const float4 *>(qrow + 32 * ks + 4);
       }
     }
-    if constexpr (Geo::kPrefetch)
-      load_tile<HD>(tb, kseq, vseq, row_bytes, t0 + step, hi32, lo_off);
+    TileRegs<HD, TR> ta, tb;
+    load_tile<HD, TR, KL>(ta, kseq, vseq, row_bytes, t0, hi32, lo_off);
     half8 qf[Geo::KS];
 #pragma unroll
     for (int ks = 0; ks < Geo::KS; ++ks) {
@@ -448,38 +527,43 @@ partial_mfma_kernel(PartialArgs a) {
         qf[ks][e] = col_valid ? val : (_Float16)0.0f;
       }
     }
+    // Only tiles with rows are loaded: even loads past the record limit
+    // (which return zeros without touching memory) cost address-unit time.
+    if constexpr (Geo::kPrefetch) {
+      if (t0 + step < hi32)
+        load_tile<HD, TR, KL>(tb, kseq, vseq, row_bytes, t0 + step, hi32, lo_off);
+    }
 
     // a4 + a5 over this wave's tiles. Double-buffered where the registers
-    // allow (head_dim <= 128): two tiles are always in flight, the one being
-    // computed and the next. At head_dim 256 one tile already holds 128 VGPRs
-    // of K/V and the occupancy is one wave per SIMD, so tiles go one at a
-    // time.
+    // allow (a tile of at most 64 VGPRs of K/V, every head_dim at 16 rows):
+    // two tiles are always in flight, the one being computed and the next;
+    // larger tiles go one at a time.
     if constexpr (Geo::kPrefetch) {
       // invariant: ta holds tile t0, tb holds tile t0 + step
       while (true) {
         const uint32_t t1 = t0 + step;
-        compute_tile<HD, (R > 1)>(ta, t0, mask32, lim32, qf, oacc, m_run, m_true, s_run, vlds, col, grp,
+        compute_tile<HD, TR, KL, (R > 1)>(ta, t0, mask32, lim32, qf, oacc, m_run, m_true, s_run, vlds, col, grp,
                          lane, hi_col);
         if (t1 >= hi32) break;
         // Inside the loop the next tile is loaded only if it has rows: even
         // zero-limit loads cost address-unit time, and a wave often has just
         // a few tiles.
         if (t1 + step < hi32)
-          load_tile<HD>(ta, kseq, vseq, row_bytes, t1 + step, hi32, lo_off);
-        compute_tile<HD, (R > 1)>(tb, t1, mask32, lim32, qf, oacc, m_run, m_true, s_run, vlds, col, grp,
+          load_tile<HD, TR, KL>(ta, kseq, vseq, row_bytes, t1 + step, hi32, lo_off);
+        compute_tile<HD, TR, KL, (R > 1)>(tb, t1, mask32, lim32, qf, oacc, m_run, m_true, s_run, vlds, col, grp,
                          lane, hi_col);
         t0 = t1 + step;
         if (t0 >= hi32) break;
         if (t0 + step < hi32)
-          load_tile<HD>(tb, kseq, vseq, row_bytes, t0 + step, hi32, lo_off);
+          load_tile<HD, TR, KL>(tb, kseq, vseq, row_bytes, t0 + step, hi32, lo_off);
       }
     } else {
       while (true) {
-        compute_tile<HD, (R > 1)>(ta, t0, mask32, lim32, qf, oacc, m_run, m_true, s_run, vlds, col, grp,
+        compute_tile<HD, TR, KL, (R > 1)>(ta, t0, mask32, lim32, qf, oacc, m_run, m_true, s_run, vlds, col, grp,
                          lane, hi_col);
         t0 += step;
         if (t0 >= hi32) break;
-        load_tile<HD>(ta, kseq, vseq, row_bytes, t0, hi32, lo_off);
+        load_tile<HD, TR, KL>(ta, kseq, vseq, row_bytes, t0, hi32, lo_off);
       }
     }
   }
@@ -495,13 +579,14 @@ partial_mfma_kernel(PartialArgs a) {
     sm_t[wave][col] = m_true;
     sm_s[wave][col] = s_run;
   }
+  wave_lds_fence();  // the slice's last tile reads come first
 #pragma unroll
   for (int i = 0; i < Geo::DB; ++i) {
     float o4[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) o4[r] = add_ror8(oacc[i][r]);
     if (col < NC)
-      *reinterpret_cast<float4 *>(&sm_o[wave][col][16 * i + 4 * grp]) =
+      *reinterpret_cast<float4 *>(vlds + (col * HD + 16 * i + 4 * grp) * 4) =
           make_float4(o4[0], o4[1], o4[2], o4[3]);
   }
   __syncthreads();
@@ -523,7 +608,8 @@ partial_mfma_kernel(PartialArgs a) {
     for (int w = 0; w < kWaves; ++w) {
       const float mw = sm_m[w][gg];
       const float c = (mw == neg_inf()) ? 0.0f : fast_exp2(mw - mm);
-      const float4 x = *reinterpret_cast<const float4 *>(&sm_o[w][gg][4 * d4]);
+      const float4 x = *reinterpret_cast<const float4 *>(
+          sm_v + w * SLICE + (gg * HD + 4 * d4) * 4);
       acc.x = fmaf(c, x.x, acc.x);
       acc.y = fmaf(c, x.y, acc.y);
       acc.z = fmaf(c, x.z, acc.z);
