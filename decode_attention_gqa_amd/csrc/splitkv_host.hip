@@ -153,8 +153,8 @@ int splitkv_workgroups_per_cu(int head_dim, int group) {
     case 8: { static const int t[8] = {4, 4, 3, 3, 2, 2, 2, 2}; return t[group - 1]; }
     case 16: { static const int t[8] = {4, 3, 3, 2, 2, 2, 2, 1}; return t[group - 1]; }
     case 32: { static const int t[8] = {4, 3, 3, 2, 2, 2, 2, 1}; return t[group - 1]; }
-    case 64: return 5;
-    case 128: return 3;
+    case 64: return 7;
+    case 128: return 4;
     case 256: return 2;
     default: return 0;
   }

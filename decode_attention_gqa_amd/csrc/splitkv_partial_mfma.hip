@@ -28,28 +28,28 @@
 // MFMA computes both halves and a DPP row rotation by 8 adds them.
 //
 // Data flow of one wave over a tile of 16 rows (a workgroup's waves take
-// interleaved tiles; the next tile's loads are issued before the current tile
-// is computed, so two tiles per wave are in flight):
-//   K, V: 16-byte loads that each cover whole 256-byte rows (one instruction
-//      = 64 lanes = 4 rows of hd 128), so every cache line a load touches is
-//      used in full. A load pattern shaped like the MFMA operand (16 rows x
-//      64 bytes per instruction, two instructions per line) measured ~1.2 us
-//      slower per 64 MB launch;
-//   K: written row-major into the wave's LDS slice (rows 16 bytes past a
-//      multiple of 256, so the 16 rows of an operand read hit 16 different
-//      bank groups) and read back as the A operand of S = K·Q'ᵀ: lane l holds
-//      row l % 16, dims 32*ks + 8*(l/16);
+// interleaved tiles):
+//   loads: K and V with 16-byte loads that each cover whole 2*hd-byte rows
+//      (one instruction = 64 lanes = 4 rows at hd 128), so every cache line
+//      an instruction touches is used in full. (A K load shaped like the
+//      MFMA operand, 16 rows x 64 bytes per instruction, measured ~1.2 us
+//      slower per 64 MB launch.)
+//   staging: the tile's K and V rows go from the load registers into the
+//      wave's LDS slice; the next tile's loads are issued into the same
+//      registers once the staged tile is computed (one tile per wave in
+//      flight at most: fewer bytes queued in the memory system measured
+//      faster than keeping every wave's next tile in flight).
+//   K: LDS rows 16 bytes past a multiple of 256 bytes apart, so the 16 rows
+//      of an operand read fall in 16 different bank groups; read back as the
+//      A operand of S = K·Q'ᵀ: lane l holds row l % 16, dims 32*ks + 8*(l/16);
 //   scores: D lane l holds rows 4*(l/16)+r of its column l % 16 -> max over
 //      the tile by in-lane max and two cross-group exchanges,
 //      p = exp2(s - m);
 //   p: already in the B-operand layout of O += Vᵀ·P (4 rows per lane);
-//   V: written row-major into the wave's LDS slice (rows padded by 32 bytes
-//      against bank conflicts), read back with the gfx950 transposing LDS
-//      read (ds_read_b64_tr_b16), which delivers four rows of one dim per
-//      lane: the A operand of Vᵀ·P on v_mfma_f32_16x16x16_f16.
-// The kernel template also builds 32- and 64-row tiles (k = 32 MFMA for the
-// output) and the operand-shaped K loads for A/B measurements; the launched
-// form is 16 rows with K through LDS.
+//   V: LDS rows padded by 32 bytes against bank conflicts, read back with
+//      the gfx950 transposing LDS read (ds_read_b64_tr_b16), which delivers
+//      four rows of one dim per lane: the A operand of Vᵀ·P on
+//      v_mfma_f32_16x16x16_f16.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -74,29 +74,30 @@ typedef __attribute__((address_space(3))) short4v lds_short4v;
 constexpr int kRor8 = 0x128;  // DPP row_ror:8 (rotate by 8 within 16 lanes)
 constexpr float kLazyLog2 = 8.0f;  // reference-max lag allowed (base-2 units)
 
-template <int HD, int TR>
+constexpr int kTileRows = 16;
+
+template <int HD>
 struct MGeo {
   static constexpr int KS = HD / 32;               // q·k k-steps of 32 dims
   static constexpr int DB = HD / 16;               // p·v output blocks of 16 dims
-  static constexpr int LPR = HD / 8;               // lanes per row (V staging)
-  static constexpr int RPI = 64 / LPR;             // rows per staging load
-  static constexpr int RG = TR / 16;               // 16-row groups per tile
-  static constexpr int NV = TR / RPI;              // staging loads per tile
-  static constexpr int VSTR = HD * 2 + 32;         // LDS bytes per staged row
-  static constexpr int VR = TR < 32 ? TR : 32;     // rows staged at a time
-  static constexpr int VTILE = VR * VSTR;          // LDS bytes of staged V
+  static constexpr int LPR = HD / 8;               // lanes per row in a load
+  static constexpr int RPI = 64 / LPR;             // rows per load instruction
+  static constexpr int NL = kTileRows / RPI;       // loads per tile and tensor
   static constexpr int KSTR = HD * 2 + 16;         // LDS bytes per staged K row
-  static constexpr int KTILE = TR * KSTR;          // LDS bytes of staged K
-  // two tiles in registers when a tile holds at most 64 VGPRs of K/V
-  static constexpr bool kPrefetch = HD * TR <= 128 * 32;
+  static constexpr int VSTR = HD * 2 + 32;         // LDS bytes per staged V row
+  static constexpr int KTILE = kTileRows * KSTR;   // staged K bytes
+  // LDS bytes per wave: staged K and V; after the last tile the same bytes
+  // hold the wave's unnormalised output for the workgroup merge.
+  static constexpr int SLICE = KTILE + kTileRows * VSTR;
   static_assert(HD % 32 == 0 && HD <= 256, "head_dim");
-  static_assert(TR == 16 || TR == 32 || TR == 64, "tile rows");
 };
 
-template <int HD, int TR>
+// One tile's K and V rows as loaded: load i holds rows RPI*i + lane / LPR,
+// dims 8*(lane % LPR) .. +7.
+template <int HD>
 struct TileRegs {
-  uint4 k[MGeo<HD, TR>::RG][MGeo<HD, TR>::KS];
-  uint4 v[MGeo<HD, TR>::NV];
+  uint4 k[MGeo<HD>::NL];
+  uint4 v[MGeo<HD>::NL];
 };
 
 __device__ __forceinline__ half8 as_half8(const uint4 &u) {
@@ -161,25 +162,14 @@ __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) 
   return make_uint4(x[0], x[1], x[2], x[3]);
 }
 
-// Per-lane byte offsets of the loads, the same for every row group: K lane l
-// reads row l % 16 of its 16-row group at dims 8*(l/16) (+ 32*ks dims through
-// the instruction offset); V lane l reads row l / LPR of its RPI-row group at
-// dims 8*(l % LPR). row_bytes = n_kv_head * HD * 2.
-struct LaneOffsets {
-  uint32_t k;
-  uint32_t v;
-};
-
+// Per-lane byte offset of the loads, the same for every instruction: lane l
+// reads row l / LPR of its RPI-row group at dims 8*(l % LPR).
+// row_bytes = n_kv_head * HD * 2.
 template <int HD>
-__device__ __forceinline__ LaneOffsets lane_offsets(uint32_t row_bytes,
-                                                    int col, int grp,
-                                                    int lane) {
-  using Geo = MGeo<HD, 16>;
-  LaneOffsets o;
-  o.k = (uint32_t)col * row_bytes + 16u * grp;
-  o.v = (uint32_t)(lane / Geo::LPR) * row_bytes +
-        16u * (uint32_t)(lane % Geo::LPR);
-  return o;
+__device__ __forceinline__ uint32_t lane_offset(uint32_t row_bytes, int lane) {
+  using Geo = MGeo<HD>;
+  return (uint32_t)(lane / Geo::LPR) * row_bytes +
+         16u * (uint32_t)(lane % Geo::LPR);
 }
 
 // Raw buffer view of rows [first, hi) of one (sequence, KV head) cache slice:
@@ -194,109 +184,74 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_view(
       limit, kBufferWord3);
 }
 
-// Issue the loads of the TR-row tile starting at row tb (tb < hi).
-template <int HD, int TR, bool KL>
-__device__ __forceinline__ void load_tile(TileRegs<HD, TR> &t,
-                                          const uint16_t *kseq,
+// Issue the loads of the 16-row tile starting at row tb (tb < hi).
+template <int HD>
+__device__ __forceinline__ void load_tile(TileRegs<HD> &t, const uint16_t *kseq,
                                           const uint16_t *vseq,
                                           uint32_t row_bytes, uint32_t tb,
-                                          uint32_t hi, const LaneOffsets &o) {
-  using Geo = MGeo<HD, TR>;
-  if constexpr (KL) {
-    // whole rows, as for V: instruction i covers rows RPI*i .. RPI*i + RPI-1
+                                          uint32_t hi, uint32_t off) {
+  using Geo = MGeo<HD>;
+  // all K first: the scores need only K, and loads return in order
 #pragma unroll
-    for (int i = 0; i < Geo::RG * Geo::KS; ++i) {
-      const __amdgpu_buffer_rsrc_t r =
-          rows_view(kseq, row_bytes, tb + (uint32_t)(Geo::RPI * i), hi);
-      t.k[i / Geo::KS][i % Geo::KS] = load16(r, o.v);
-    }
-  } else {
+  for (int i = 0; i < Geo::NL; ++i)
+    t.k[i] = load16(rows_view(kseq, row_bytes, tb + (uint32_t)(Geo::RPI * i), hi), off);
 #pragma unroll
-    for (int rt = 0; rt < Geo::RG; ++rt) {
-      const __amdgpu_buffer_rsrc_t r = rows_view(kseq, row_bytes, tb + 16u * rt, hi);
-#pragma unroll
-      for (int ks = 0; ks < Geo::KS; ++ks) t.k[rt][ks] = load16(r, o.k + 64u * ks);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < Geo::NV; ++i) {
-    const __amdgpu_buffer_rsrc_t r =
-        rows_view(vseq, row_bytes, tb + (uint32_t)(Geo::RPI * i), hi);
-    t.v[i] = load16(r, o.v);
-  }
+  for (int i = 0; i < Geo::NL; ++i)
+    t.v[i] = load16(rows_view(vseq, row_bytes, tb + (uint32_t)(Geo::RPI * i), hi), off);
 }
 
-// mask_from: wave-uniform row from which some column may be masked; lim: this
-// lane's column's end row (equal to mask_from with one query row per
-// workgroup). SAFE: a column may have no live row yet (several query rows per
-// workgroup), so -inf maxima are guarded.
-template <int HD, int TR, bool KL, bool SAFE>
+// Write a loaded tile's K (or V) rows into the wave's LDS slice, row-major
+// with a pitch of STR bytes. The fences order these writes after the
+// previous reads of the same bytes.
+template <int HD, int STR>
+__device__ __forceinline__ void stage_rows(const uint4 (&x)[MGeo<HD>::NL],
+                                           unsigned char *dst, int lane) {
+  using Geo = MGeo<HD>;
+  wave_lds_fence();
+#pragma unroll
+  for (int i = 0; i < Geo::NL; ++i)
+    *reinterpret_cast<uint4 *>(dst + (Geo::RPI * i + lane / Geo::LPR) * STR +
+                               16 * (lane % Geo::LPR)) = x[i];
+  wave_lds_fence();
+}
+
+// a4 + a5 for the loaded tile starting at row tb. mask_from: wave-uniform row
+// from which some column may be masked; lim: this lane's column's end row
+// (equal to mask_from with one query row per workgroup). SAFE: a column may
+// have no live row yet (several query rows per workgroup), so -inf maxima are
+// guarded. K is staged first and V only after the softmax, so the V rows
+// (which arrive last) are written while the exponentials run.
+template <int HD, bool SAFE>
 __device__ __forceinline__ void compute_tile(
-    const TileRegs<HD, TR> &t, uint32_t tb, uint32_t mask_from, uint32_t lim,
-    const half8 (&qf)[MGeo<HD, TR>::KS], float4v (&oacc)[MGeo<HD, TR>::DB],
-    float &m_run, float &m_true, float &s_run, unsigned char *slice, int col,
-    int grp, int lane, bool hi_col) {
-  using Geo = MGeo<HD, TR>;
-  constexpr int RG = Geo::RG;
-  unsigned char *vlds = slice + (KL ? Geo::KTILE : 0);
-  // K operands: straight from the loads, or (KL) whole rows through LDS:
-  // written row-major with KSTR-byte rows, read back as lane l = row l % 16,
-  // dims 32*ks + 8*(l/16) (row pitch 16 bytes past a multiple of 256: the 16
-  // rows of a read fall in 16 different bank groups).
-  uint4 ka[RG][Geo::KS];
-  if constexpr (KL) {
-    wave_lds_fence();
+    const TileRegs<HD> &t, unsigned char *slice, uint32_t tb,
+    uint32_t mask_from, uint32_t lim, const half8 (&qf)[MGeo<HD>::KS],
+    float4v (&oacc)[MGeo<HD>::DB], float &m_run, float &m_true, float &s_run,
+    int col, int grp, int lane, bool hi_col) {
+  using Geo = MGeo<HD>;
+  unsigned char *vlds = slice + Geo::KTILE;
+  // a4: scores S = K · Q'ᵀ, K operands read back from the staged rows.
+  stage_rows<HD, Geo::KSTR>(t.k, slice, lane);
+  uint4 ka[Geo::KS];
 #pragma unroll
-    for (int i = 0; i < RG * Geo::KS; ++i) {
-      const int rl = Geo::RPI * i + lane / Geo::LPR;
-      *reinterpret_cast<uint4 *>(slice + rl * Geo::KSTR +
-                                 16 * (lane % Geo::LPR)) = t.k[i / Geo::KS][i % Geo::KS];
-    }
-    wave_lds_fence();
+  for (int ks = 0; ks < Geo::KS; ++ks)
+    ka[ks] = *reinterpret_cast<const uint4 *>(slice + col * Geo::KSTR +
+                                               64 * ks + 16 * grp);
+  float4v sc = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int rt = 0; rt < RG; ++rt)
-#pragma unroll
-      for (int ks = 0; ks < Geo::KS; ++ks)
-        ka[rt][ks] = *reinterpret_cast<const uint4 *>(
-            slice + (16 * rt + col) * Geo::KSTR + 64 * ks + 16 * grp);
-  } else {
-#pragma unroll
-    for (int rt = 0; rt < RG; ++rt)
-#pragma unroll
-      for (int ks = 0; ks < Geo::KS; ++ks) ka[rt][ks] = t.k[rt][ks];
-  }
-  // a4: scores S = K · Q'ᵀ for the tile's 16-row groups.
-  float4v sc[RG];
-#pragma unroll
-  for (int rt = 0; rt < RG; ++rt) {
-    sc[rt] = float4v{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < Geo::KS; ++ks)
-      sc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(ka[rt][ks]),
-                                                      qf[ks], sc[rt], 0, 0, 0);
-  }
+  for (int ks = 0; ks < Geo::KS; ++ks)
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(ka[ks]), qf[ks], sc,
+                                                0, 0, 0);
   // hi + lo columns; rows at or past the column's end (last tiles only) score
   // -inf.
-  float s[RG][4];
+  float s[4];
 #pragma unroll
-  for (int rt = 0; rt < RG; ++rt) {
+  for (int r = 0; r < 4; ++r) s[r] = add_ror8(sc[r]);
+  if (tb + kTileRows > mask_from) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) s[rt][r] = add_ror8(sc[rt][r]);
+    for (int r = 0; r < 4; ++r)
+      if (tb + (uint32_t)(4 * grp + r) >= lim) s[r] = neg_inf();
   }
-  if (tb + TR > mask_from) {
-#pragma unroll
-    for (int rt = 0; rt < RG; ++rt) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r)
-        if (tb + (uint32_t)(16 * rt + 4 * grp + r) >= lim) s[rt][r] = neg_inf();
-    }
-  }
-  float mt = neg_inf();
-#pragma unroll
-  for (int rt = 0; rt < RG; ++rt) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) mt = fmaxf(mt, s[rt][r]);
-  }
+  float mt = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3]));
   mt = pair32_max(pair16_max(mt));
   // a5: online softmax against a reference max m_run that moves only when a
   // tile's max exceeds it by more than kLazyLog2 (and always from -inf; the
@@ -312,26 +267,16 @@ __device__ __forceinline__ void compute_tile(
   const float corr = (SAFE && m_run == neg_inf()) ? 0.0f : fast_exp2(m_run - mn);
   const float mref = (SAFE && mn == neg_inf()) ? 0.0f : mn;
   // p hi or lo parts in this lane's rows: the B operand of O += Vᵀ·P
-  _Float16 pf[4 * RG];
-  float pv[4 * RG];
+  half4 pf;
+  float pv[4];
 #pragma unroll
-  for (int rt = 0; rt < RG; ++rt) {
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float p = fast_exp2(s[rt][r] - mref);  // exp2(-inf) = 0
-      pv[4 * rt + r] = p;
-      const _Float16 h = (_Float16)p;
-      pf[4 * rt + r] = hi_col ? h : (_Float16)(p - (float)h);
-    }
+  for (int r = 0; r < 4; ++r) {
+    const float p = fast_exp2(s[r] - mref);  // exp2(-inf) = 0
+    pv[r] = p;
+    const _Float16 h = (_Float16)p;
+    pf[r] = hi_col ? h : (_Float16)(p - (float)h);
   }
-  // the tile's weight sum as a tree (no long dependent chain)
-  float psum4[RG];
-#pragma unroll
-  for (int rt = 0; rt < RG; ++rt)
-    psum4[rt] = (pv[4 * rt] + pv[4 * rt + 1]) + (pv[4 * rt + 2] + pv[4 * rt + 3]);
-  float psum = psum4[0];
-  if constexpr (RG == 2) psum = psum4[0] + psum4[1];
-  if constexpr (RG == 4) psum = (psum4[0] + psum4[1]) + (psum4[2] + psum4[3]);
+  const float psum = (pv[0] + pv[1]) + (pv[2] + pv[3]);
   // Rescale only when some column's reference moved (else corr is 1 for
   // every column and the products would change nothing).
   if (__any(mn != m_run)) {
@@ -342,50 +287,19 @@ __device__ __forceinline__ void compute_tile(
   s_run += psum;
   m_run = mn;
 
-  // O += Vᵀ · P, 32 rows (16 with one row group) at a time: the V rows go
-  // into this wave's LDS slice, row-major with padded rows, and lane
-  // (grp, col) reads back dim 16b + col of rows 4*grp + 0..3 and
-  // 16 + 4*grp + 0..3, the same row order as its p values. One row group:
-  // the k = 16 MFMA; otherwise the k = 32 MFMA per 32 rows.
+  // O += Vᵀ · P: lane (grp, col) reads dim 16b + col of rows 4*grp + 0..3,
+  // the same row order as its p values.
+  stage_rows<HD, Geo::VSTR>(t.v, vlds, lane);
   const int c4 = col >> 2;
   const int cm = col & 3;
-  constexpr int NH = RG >= 2 ? RG / 2 : 1;    // 32-row halves
-  constexpr int NVH = Geo::NV / NH;           // staging loads per half
 #pragma unroll
-  for (int h = 0; h < NH; ++h) {
-    wave_lds_fence();
-#pragma unroll
-    for (int i = 0; i < NVH; ++i) {
-      const int rl = Geo::RPI * i + lane / Geo::LPR;
-      *reinterpret_cast<uint4 *>(vlds + rl * Geo::VSTR +
-                                 16 * (lane % Geo::LPR)) = t.v[NVH * h + i];
-    }
-    wave_lds_fence();
-#pragma unroll
-    for (int b = 0; b < Geo::DB; ++b) {
-      const int byte_col = (16 * b + 4 * cm) * 2;
-      // (C-style casts: address-space conversion of the generic LDS pointer)
-      lds_short4v *a0 =
-          (lds_short4v *)(vlds + (4 * grp + c4) * Geo::VSTR + byte_col);
-      const short4v r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(a0);
-      if constexpr (RG >= 2) {
-        lds_short4v *a1 =
-            (lds_short4v *)(vlds + (16 + 4 * grp + c4) * Geo::VSTR + byte_col);
-        const short4v r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(a1);
-        const half8 vf = __builtin_shufflevector(__builtin_bit_cast(half4, r0),
-                                                 __builtin_bit_cast(half4, r1),
-                                                 0, 1, 2, 3, 4, 5, 6, 7);
-        const half8 pb = {pf[8 * h], pf[8 * h + 1], pf[8 * h + 2],
-                          pf[8 * h + 3], pf[8 * h + 4], pf[8 * h + 5],
-                          pf[8 * h + 6], pf[8 * h + 7]};
-        oacc[b] =
-            __builtin_amdgcn_mfma_f32_16x16x32_f16(vf, pb, oacc[b], 0, 0, 0);
-      } else {
-        const half4 pb = {pf[0], pf[1], pf[2], pf[3]};
-        oacc[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-            __builtin_bit_cast(half4, r0), pb, oacc[b], 0, 0, 0);
-      }
-    }
+  for (int b = 0; b < Geo::DB; ++b) {
+    // (C-style cast: address-space conversion of the generic LDS pointer)
+    lds_short4v *a0 = (lds_short4v *)(vlds + (4 * grp + c4) * Geo::VSTR +
+                                      (16 * b + 4 * cm) * 2);
+    const short4v r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(a0);
+    oacc[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+        __builtin_bit_cast(half4, r0), pf, oacc[b], 0, 0, 0);
   }
 }
 
@@ -397,14 +311,11 @@ __device__ __forceinline__ void compute_tile(
 // R: query rows per workgroup (several query rows per sequence). The MFMA
 // columns then hold (row, head) pairs, column c = r * G + g, so every K/V row
 // is read once for the R rows; with R = 1 each workgroup serves one row.
-template <int HD, int G, bool PER_HEAD = false, int R = 1, int TR = 16,
-          bool KL = true>
+template <int HD, int G, bool PER_HEAD = false, int R = 1>
 __global__ __launch_bounds__(kThreads, 2) void
 partial_mfma_kernel(PartialArgs a) {
-  using Geo = MGeo<HD, TR>;
-  // LDS per wave: staged K (KL) and V; after the last tile the same bytes
-  // hold the wave's unnormalised output for the workgroup merge.
-  constexpr int SLICE = (KL ? Geo::KTILE : 0) + Geo::VTILE;
+  using Geo = MGeo<HD>;
+  constexpr int SLICE = Geo::SLICE;
   constexpr int NC = G * R;                          // MFMA columns in use
   static_assert(G >= 1 && G <= 8 && NC <= 8, "group x rows");
   static_assert(!PER_HEAD || (G == 1 && R == 1), "per-head form: one head");
@@ -468,13 +379,13 @@ partial_mfma_kernel(PartialArgs a) {
   const size_t seq_base = ((size_t)b * (size_t)a.max_ctx * a.n_kv_head + hk) * HD;
   const uint16_t *kseq = a.k + seq_base;
   const uint16_t *vseq = a.v + seq_base;
-  const LaneOffsets lo_off = lane_offsets<HD>(row_bytes, col, grp, lane);
-  unsigned char *vlds = sm_v + wave * SLICE;
+  const uint32_t off = lane_offset<HD>(row_bytes, lane);
+  unsigned char *slice = sm_v + wave * SLICE;
   const uint32_t hi32 = (uint32_t)hi;
   const uint32_t mask32 = (uint32_t)mask_from;
   const uint32_t lim32 = (uint32_t)col_end;
-  const uint32_t step = (uint32_t)(kWaves * TR);
-  uint32_t t0 = (uint32_t)lo + (uint32_t)(wave * TR);
+  const uint32_t step = (uint32_t)(kWaves * kTileRows);
+  uint32_t t0 = (uint32_t)lo + (uint32_t)(wave * kTileRows);
   if (lo >= hi) t0 = hi32;  // idle split
 
   float4v oacc[Geo::DB];
@@ -487,12 +398,9 @@ partial_mfma_kernel(PartialArgs a) {
   // A wave whose first tile starts at or past hi has no rows: it keeps the
   // empty state (-inf, 0, 0) and issues no loads at all.
   if (t0 < hi32) {
-    // Issue order: the queries, the first tile's K/V, the query conversion
-    // (it waits for the query loads only, which come back while the tile is
-    // in flight), then the second tile. Delaying the second tile by the
-    // conversion lets the first tiles of all resident waves reach the memory
-    // queues ahead of any second tile, so first tiles land early and their
-    // compute overlaps the rest of the stream.
+    // Issue order: the queries, then the first tile. The query conversion
+    // waits for the query loads only, which come back while the tile is in
+    // flight.
     //
     // a3: B operand of S = K·Q'ᵀ: column col holds (row, head) col % 8, hi
     // part in columns 0..7 and lo part in 8..15 (zero for unused columns),
@@ -508,8 +416,8 @@ partial_mfma_kernel(PartialArgs a) {
         qraw[ks][1] = *reinterpret_cast<const float4 *>(qrow + 32 * ks + 4);
       }
     }
-    TileRegs<HD, TR> ta, tb;
-    load_tile<HD, TR, KL>(ta, kseq, vseq, row_bytes, t0, hi32, lo_off);
+    TileRegs<HD> tr;
+    load_tile<HD>(tr, kseq, vseq, row_bytes, t0, hi32, off);
     half8 qf[Geo::KS];
 #pragma unroll
     for (int ks = 0; ks < Geo::KS; ++ks) {
@@ -527,44 +435,22 @@ partial_mfma_kernel(PartialArgs a) {
         qf[ks][e] = col_valid ? val : (_Float16)0.0f;
       }
     }
-    // Only tiles with rows are loaded: even loads past the record limit
-    // (which return zeros without touching memory) cost address-unit time.
-    if constexpr (Geo::kPrefetch) {
-      if (t0 + step < hi32)
-        load_tile<HD, TR, KL>(tb, kseq, vseq, row_bytes, t0 + step, hi32, lo_off);
-    }
 
-    // a4 + a5 over this wave's tiles. Double-buffered where the registers
-    // allow (a tile of at most 64 VGPRs of K/V, every head_dim at 16 rows):
-    // two tiles are always in flight, the one being computed and the next;
-    // larger tiles go one at a time.
-    if constexpr (Geo::kPrefetch) {
-      // invariant: ta holds tile t0, tb holds tile t0 + step
-      while (true) {
-        const uint32_t t1 = t0 + step;
-        compute_tile<HD, TR, KL, (R > 1)>(ta, t0, mask32, lim32, qf, oacc, m_run, m_true, s_run, vlds, col, grp,
-                         lane, hi_col);
-        if (t1 >= hi32) break;
-        // Inside the loop the next tile is loaded only if it has rows: even
-        // zero-limit loads cost address-unit time, and a wave often has just
-        // a few tiles.
-        if (t1 + step < hi32)
-          load_tile<HD, TR, KL>(ta, kseq, vseq, row_bytes, t1 + step, hi32, lo_off);
-        compute_tile<HD, TR, KL, (R > 1)>(tb, t1, mask32, lim32, qf, oacc, m_run, m_true, s_run, vlds, col, grp,
-                         lane, hi_col);
-        t0 = t1 + step;
-        if (t0 >= hi32) break;
-        if (t0 + step < hi32)
-          load_tile<HD, TR, KL>(tb, kseq, vseq, row_bytes, t0 + step, hi32, lo_off);
-      }
-    } else {
-      while (true) {
-        compute_tile<HD, TR, KL, (R > 1)>(ta, t0, mask32, lim32, qf, oacc, m_run, m_true, s_run, vlds, col, grp,
-                         lane, hi_col);
-        t0 += step;
-        if (t0 >= hi32) break;
-        load_tile<HD, TR, KL>(ta, kseq, vseq, row_bytes, t0, hi32, lo_off);
-      }
+    // a4 + a5 over this wave's tiles: compute the landed tile (staged
+    // through LDS), then issue the next tile's loads (only tiles with rows:
+    // even loads past the record limit, which return zeros without touching
+    // memory, cost address-unit time). Each wave has at most one tile in
+    // flight, and none while it computes: at 32K rows, issuing the next tile
+    // before computing the current one (one more tile in flight per wave)
+    // measured 0.4 us per layer slower, and a second register tile 0.6 us,
+    // because deeper memory queues serve the workgroups dispatched last later
+    // still.
+    while (true) {
+      compute_tile<HD, (R > 1)>(tr, slice, t0, mask32, lim32, qf, oacc, m_run,
+                                m_true, s_run, col, grp, lane, hi_col);
+      t0 += step;
+      if (t0 >= hi32) break;
+      load_tile<HD>(tr, kseq, vseq, row_bytes, t0, hi32, off);
     }
   }
 
@@ -586,7 +472,7 @@ partial_mfma_kernel(PartialArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) o4[r] = add_ror8(oacc[i][r]);
     if (col < NC)
-      *reinterpret_cast<float4 *>(vlds + (col * HD + 16 * i + 4 * grp) * 4) =
+      *reinterpret_cast<float4 *>(slice + (col * HD + 16 * i + 4 * grp) * 4) =
           make_float4(o4[0], o4[1], o4[2], o4[3]);
   }
   __syncthreads();
