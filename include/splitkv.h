@@ -106,8 +106,10 @@ int splitkv_workgroups_per_cu(int head_dim, int group);
  * write, merge) stay small ("10 · R4", section 3.3; "Red Lite dev35", the
  * block-length table). The rule:
  *   fill = floor(wpc * cu_count / (batch * n_kv_head)), wpc from
- *          splitkv_workgroups_per_cu: one full round of resident workgroups,
- *          never a partial second round;
+ *          splitkv_workgroups_per_cu, capped at 256 / head_dim for head_dim
+ *          >= 64 (the matrix-core kernel: more resident workgroups only add
+ *          per-split fixed costs there, measured): one full round of
+ *          resident workgroups, never a partial second round;
  *   bal  = min(ceil(16 * cu_count / (batch * n_kv_head)), max_ctx / 1024)
  *          when batch > 1, else 0: with several sequences (lengths unknown
  *          to the host) about 16 workgroups per compute unit balance uneven
