@@ -651,8 +651,10 @@ def run_per_head(args):
     max_ctx = synth.CFG3.max_ctx
     S_g, _ = skv.pick_splits(1, 28, 4, 128, max_ctx, cu)
     variants = [("grouped", S_g)] + [("per_head", s) for s in args.sweep_splits]
+    case = None
     for form, S in variants:
-        lay = Layers(args.layers, max_ctx, S, 0)
+        lay = Layers(args.layers, max_ctx, S, 0, case=case)
+        case = lay.case
         part_fn = skv.partial if form == "grouped" else skv.partial_per_head
 
         def step():
