@@ -39,16 +39,22 @@ struct SplitRange {
   long long hi;
 };
 
+// Every value fits in 32 bits: nkv <= max_ctx < 2^31; with a fixed block
+// length the host checks block_len * n_splits <= INT_MAX, and otherwise
+// (sp + 1) * chunk < nkv + n_splits. (This runs between the live-length load
+// and the first K/V load of every workgroup, so it avoids 64-bit division.)
 __device__ __forceinline__ SplitRange split_range(const PartialArgs &a,
                                                   int sp, int b) {
-  long long nkv = (long long)a.positions[b] + 1;
-  nkv = nkv < 0 ? 0 : (nkv > a.max_ctx ? a.max_ctx : nkv);
-  const long long chunk =
-      a.block_len > 0 ? (long long)a.block_len
-                      : (nkv + a.n_splits - 1) / a.n_splits;
+  const int p = a.positions[b];
+  const uint32_t mc = (uint32_t)a.max_ctx;
+  const uint32_t nkv = p < 0 ? 0u : ((uint32_t)p >= mc ? mc : (uint32_t)p + 1u);
+  const uint32_t ns = (uint32_t)a.n_splits;
+  const uint32_t chunk =
+      a.block_len > 0 ? (uint32_t)a.block_len : (nkv + ns - 1u) / ns;
+  const uint32_t lo = (uint32_t)sp * chunk;
+  const uint32_t h = lo + chunk;
   SplitRange r;
-  r.lo = (long long)sp * chunk;
-  const long long h = r.lo + chunk;
+  r.lo = lo;
   r.hi = h < nkv ? h : nkv;
   return r;
 }

@@ -184,6 +184,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_view(
       limit, kBufferWord3);
 }
 
+// Workgroup barrier that orders LDS accesses only (no wait for outstanding
+// global loads).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// s_waitcnt immediate for "at most n vector memory loads outstanding" (gfx9
+// encoding: vmcnt in bits 3:0 and 15:14; expcnt and lgkmcnt left at their
+// maxima, i.e. not waited for).
+constexpr int vmcnt_imm(int n) {
+  return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
+}
+
 // Issue the loads of the 16-row tile starting at row tb (tb < hi).
 template <int HD>
 __device__ __forceinline__ void load_tile(TileRegs<HD> &t, const uint16_t *kseq,
@@ -191,6 +206,11 @@ __device__ __forceinline__ void load_tile(TileRegs<HD> &t, const uint16_t *kseq,
                                           uint32_t row_bytes, uint32_t tb,
                                           uint32_t hi, uint32_t off) {
   using Geo = MGeo<HD>;
+  // tb and hi are wave-uniform; without the explicit scalar copies the
+  // compiler kept the loop's row counter in a vector register and wrapped
+  // every load in a loop over distinct descriptors
+  tb = __builtin_amdgcn_readfirstlane(tb);
+  hi = __builtin_amdgcn_readfirstlane(hi);
   // all K first: the scores need only K, and loads return in order
 #pragma unroll
   for (int i = 0; i < Geo::NL; ++i)
@@ -341,36 +361,60 @@ partial_mfma_kernel(PartialArgs a) {
   const bool hi_col = col < 8;
 
   __shared__ __attribute__((aligned(16))) unsigned char sm_v[kWaves * SLICE];
-  __shared__ float sm_m[kWaves][NC];   // each wave's reference max
-  __shared__ float sm_t[kWaves][NC];   // each wave's exact max
-  __shared__ float sm_s[kWaves][NC];
-  static_assert(NC * HD * 4 <= SLICE, "output state fits the wave's slice");
+  // each wave's state per column: (reference max, exact max, sum, unused)
+  __shared__ float4 sm_st[kWaves][NC];
+  // the query operand, converted once per workgroup (lane-major per ks)
+  __shared__ half8 sm_q[Geo::KS][64];
+  // a column's output in the wave's slice: HD floats, padded by 16 floats so
+  // that the columns start in different LDS banks
+  constexpr int OSTR = (HD + 16) * 4;
+  static_assert(NC * OSTR <= SLICE, "output state fits the wave's slice");
 
   // a1 + a2: live length and this split's rows; with several query rows,
   // a row's rows end at min(hi, its own live length). The waves run to the
   // end of the workgroup's last row; masking starts at its first row's end,
   // and each column stops at its own row's end.
-  const detail::SplitRange rg = detail::split_range(a, sp, b);
-  const long long lo = rg.lo;
   const int gq = col & 7;                            // this lane's column
-  long long hi, mask_from, col_end;
   bool col_valid;                                    // column maps to a row
   int col_t, col_g;                                  // and its (row, head)
   if constexpr (R == 1) {
-    hi = detail::row_end(a, rs, rg.hi);
-    mask_from = hi;
-    col_end = hi;
     col_valid = gq < G;
     col_t = rs.t;
     col_g = gq < G ? gq : 0;
   } else {
-    const int t_last = min(rs.t + R - 1, a.n_q - 1);
-    hi = detail::row_end_at(a, b, t_last, rg.hi);
-    mask_from = detail::row_end_at(a, b, rs.t, rg.hi);
     const int r_c = gq / G;
     col_valid = gq < NC && rs.t + r_c < a.n_q;
     col_t = col_valid ? rs.t + r_c : rs.t;
     col_g = col_valid ? gq - r_c * G : 0;
+  }
+
+  // a3: the queries do not depend on the live length, so wave 0 issues their
+  // loads before the live length is read (the other waves take the converted
+  // operand from LDS, below). Lane (grp, col) loads dims 32*ks + 8*grp .. +7
+  // of column col's (row, head).
+  float4 qraw[Geo::KS][2];
+  if (wave == 0) {
+    const detail::RowSel qs{b, col_t};
+    const float *qrow =
+        a.q + detail::q_offset(a, qs, hy * G + col_g, HD) + 8 * grp;
+#pragma unroll
+    for (int ks = 0; ks < Geo::KS; ++ks) {
+      qraw[ks][0] = *reinterpret_cast<const float4 *>(qrow + 32 * ks);
+      qraw[ks][1] = *reinterpret_cast<const float4 *>(qrow + 32 * ks + 4);
+    }
+  }
+
+  const detail::SplitRange rg = detail::split_range(a, sp, b);
+  const long long lo = rg.lo;
+  long long hi, mask_from, col_end;
+  if constexpr (R == 1) {
+    hi = detail::row_end(a, rs, rg.hi);
+    mask_from = hi;
+    col_end = hi;
+  } else {
+    const int t_last = min(rs.t + R - 1, a.n_q - 1);
+    hi = detail::row_end_at(a, b, t_last, rg.hi);
+    mask_from = detail::row_end_at(a, b, rs.t, rg.hi);
     col_end = col_valid ? detail::row_end_at(a, b, col_t, rg.hi) : hi;
   }
 
@@ -396,34 +440,20 @@ partial_mfma_kernel(PartialArgs a) {
   float s_run = 0.0f;
 
   // A wave whose first tile starts at or past hi has no rows: it keeps the
-  // empty state (-inf, 0, 0) and issues no loads at all.
-  if (t0 < hi32) {
-    // Issue order: the queries, then the first tile. The query conversion
-    // waits for the query loads only, which come back while the tile is in
-    // flight.
-    //
-    // a3: B operand of S = K·Q'ᵀ: column col holds (row, head) col % 8, hi
-    // part in columns 0..7 and lo part in 8..15 (zero for unused columns),
-    // dims 32*ks + 8*grp + e, pre-scaled to base-2 units.
-    float4 qraw[Geo::KS][2];
-    {
-      const detail::RowSel qs{b, col_t};
-      const float *qrow =
-          a.q + detail::q_offset(a, qs, hy * G + col_g, HD) + 8 * grp;
-#pragma unroll
-      for (int ks = 0; ks < Geo::KS; ++ks) {
-        qraw[ks][0] = *reinterpret_cast<const float4 *>(qrow + 32 * ks);
-        qraw[ks][1] = *reinterpret_cast<const float4 *>(qrow + 32 * ks + 4);
-      }
-    }
-    TileRegs<HD> tr;
-    load_tile<HD>(tr, kseq, vseq, row_bytes, t0, hi32, off);
-    half8 qf[Geo::KS];
+  // empty state (-inf, 0, 0) and issues no K/V loads at all.
+  // B operand of S = K·Q'ᵀ, the same in every wave: column col holds (row,
+  // head) col % 8, hi part in columns 0..7 and lo part in 8..15 (zero for
+  // unused columns), dims 32*ks + 8*grp + e, pre-scaled to base-2 units.
+  // Wave 0 converts it (its query loads come back while the first tile is in
+  // flight) and hands it to the other waves through LDS: one query read per
+  // workgroup instead of one per wave.
+  auto share_q = [&] {
 #pragma unroll
     for (int ks = 0; ks < Geo::KS; ++ks) {
       const float x[8] = {qraw[ks][0].x, qraw[ks][0].y, qraw[ks][0].z,
                           qraw[ks][0].w, qraw[ks][1].x, qraw[ks][1].y,
                           qraw[ks][1].z, qraw[ks][1].w};
+      half8 h8;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         // q' = q * scale_log2 as hi + lo: hi = fp16(q'), lo = fp16 of the
@@ -432,9 +462,33 @@ partial_mfma_kernel(PartialArgs a) {
         const _Float16 h = (_Float16)(x[e] * a.scale_log2);
         const float lo = __builtin_fmaf(x[e], a.scale_log2, -(float)h);
         const _Float16 val = hi_col ? h : (_Float16)lo;
-        qf[ks][e] = col_valid ? val : (_Float16)0.0f;
+        h8[e] = col_valid ? val : (_Float16)0.0f;
       }
+      sm_q[ks][lane] = h8;
     }
+  };
+  // Wave 0 has the split's first tile, so when it has no rows no wave has and
+  // nobody needs the operand. The busy and idle paths each pass the barrier
+  // on their own (a workgroup barrier counts waves, not call sites; every
+  // wave passes exactly one here), so that on the busy path the compiler's
+  // load counters see the query loads as older than the tile's: the
+  // conversion waits for the queries alone, and the first tile's waits are
+  // not widened to cover query loads. A busy wave other than 0 issued no
+  // query loads, and an idle wave 0 drains its unused ones; explicit waits
+  // tell the counters so (with 2 * NL tile loads issued the first returns at
+  // once). The barrier orders LDS only: the operand is the one thing shared.
+  const bool busy = t0 < hi32;
+  if (busy) {
+    TileRegs<HD> tr;
+    load_tile<HD>(tr, kseq, vseq, row_bytes, t0, hi32, off);
+    if (wave == 0)
+      share_q();
+    else
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * Geo::NL));
+    lds_barrier();
+    half8 qf[Geo::KS];
+#pragma unroll
+    for (int ks = 0; ks < Geo::KS; ++ks) qf[ks] = sm_q[ks][lane];
 
     // a4 + a5 over this wave's tiles: compute the landed tile (staged
     // through LDS), then issue the next tile's loads (only tiles with rows:
@@ -452,6 +506,9 @@ partial_mfma_kernel(PartialArgs a) {
       if (t0 >= hi32) break;
       load_tile<HD>(tr, kseq, vseq, row_bytes, t0, hi32, off);
     }
+  } else {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    lds_barrier();
   }
 
   // a6: merge the four waves and write the records. Each wave puts its state
@@ -459,12 +516,11 @@ partial_mfma_kernel(PartialArgs a) {
   // columns added), then after one barrier every thread merges one float4 of
   // one head's output over the four waves with weights exp2(m_ref - m_all),
   // m_all the largest exact max: the record is relative to the exact max.
+  // This runs after the workgroup's last data has landed, so its latency is
+  // on the kernel's critical path: all of a thread's LDS reads are issued
+  // before any of the arithmetic.
   s_run = pair32_sum(pair16_sum(s_run));
-  if (grp == 0 && col < NC) {
-    sm_m[wave][col] = m_run;
-    sm_t[wave][col] = m_true;
-    sm_s[wave][col] = s_run;
-  }
+  if (grp == 0 && col < NC) sm_st[wave][col] = make_float4(m_run, m_true, s_run, 0.f);
   wave_lds_fence();  // the slice's last tile reads come first
 #pragma unroll
   for (int i = 0; i < Geo::DB; ++i) {
@@ -472,7 +528,7 @@ partial_mfma_kernel(PartialArgs a) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) o4[r] = add_ror8(oacc[i][r]);
     if (col < NC)
-      *reinterpret_cast<float4 *>(slice + (col * HD + 16 * i + 4 * grp) * 4) =
+      *reinterpret_cast<float4 *>(slice + col * OSTR + (16 * i + 4 * grp) * 4) =
           make_float4(o4[0], o4[1], o4[2], o4[3]);
   }
   __syncthreads();
@@ -485,22 +541,27 @@ partial_mfma_kernel(PartialArgs a) {
     // column gg = (row r, head g); rows past n_q have no record
     const int r = gg / G;
     if (R > 1 && rs.t + r >= a.n_q) continue;
+    float4 stw[kWaves], x[kWaves];
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      stw[w] = sm_st[w][gg];
+      x[w] = *reinterpret_cast<const float4 *>(sm_v + w * SLICE + gg * OSTR +
+                                               16 * d4);
+    }
     float mm = neg_inf();
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, sm_t[w][gg]);
+    for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, stw[w].y);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float st = 0.0f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
-      const float mw = sm_m[w][gg];
+      const float mw = stw[w].x;
       const float c = (mw == neg_inf()) ? 0.0f : fast_exp2(mw - mm);
-      const float4 x = *reinterpret_cast<const float4 *>(
-          sm_v + w * SLICE + (gg * HD + 4 * d4) * 4);
-      acc.x = fmaf(c, x.x, acc.x);
-      acc.y = fmaf(c, x.y, acc.y);
-      acc.z = fmaf(c, x.z, acc.z);
-      acc.w = fmaf(c, x.w, acc.w);
-      st = fmaf(c, sm_s[w][gg], st);
+      acc.x = fmaf(c, x[w].x, acc.x);
+      acc.y = fmaf(c, x[w].y, acc.y);
+      acc.z = fmaf(c, x[w].z, acc.z);
+      acc.w = fmaf(c, x[w].w, acc.w);
+      st = fmaf(c, stw[w].z, st);
     }
     float *rec = rec0 + (size_t)(gg - r * G) * pstr +
                  (size_t)r * a.n_head * pstr;  // row t + r: n_head records on
