@@ -32,6 +32,7 @@ Usage: python bench.py [--steps K] [--warmup W] [--nkv N] [--layers L]
        python bench.py --mode per_head --sweep-splits 18 36 64 128
                                         # grouped vs per-query-head grid
        python bench.py --mode rows      # n_q query rows per sequence (causal)
+       python bench.py --mode long      # 28q/4kv hd128 at 16K..128K rows
        python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --kernels-json F
                                         # fold two rocprofv3 --pmc runs
 """
@@ -692,6 +693,38 @@ def run_per_head(args):
         torch.cuda.empty_cache()
 
 
+def run_long(args):
+    """The headline shape past the 32K configs: 28q/4kv hd128 with max_ctx
+    131,328, one graph of L layers x (partial + combine) replayed at live
+    lengths 16K..128K (per-layer KV 32..256 MB, every layer in its own
+    buffers), plus the partial kernel alone at each length."""
+    import torch
+
+    import decode_attention_gqa_amd as skv
+    import synth
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    max_ctx = 131072 + 256
+    S, blk = skv.pick_splits(1, 28, 4, 128, max_ctx, cu)
+    lay = Layers(args.layers, max_ctx, S, blk)
+    graph = lay.capture()
+    for nkv in (16384, 32768, 65536, 131072):
+        lay.set_nkv(nkv)
+        per, _, _ = time_replays(torch, graph, args.warmup, args.steps)
+        med = statistics.median(per)
+        kv = synth.kv_bytes(4, 128, nkv)
+        p_mean, _ = time_kernel(torch, lay.partial, lay.L, args.kernel_reps)
+        print(json.dumps({"long": True, "nkv": nkv, "max_ctx": max_ctx,
+                          "n_splits": S, "layers": lay.L,
+                          "us_per_layer": round(med * 1e3 / lay.L, 3),
+                          "kv_gbps": round(kv * lay.L / (med * 1e-3) / 1e9, 1),
+                          "pct_hbm_peak": round(100 * kv * lay.L / (med * 1e-3)
+                                                / 1e9 / HBM_PEAK_GBPS, 2),
+                          "partial_avg_us": round(p_mean * 1e3, 3),
+                          "partial_pct_hbm_peak": round(
+                              100 * kv / (p_mean * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}),
+              flush=True)
+
+
 def run_rows(args):
     """Several query rows per sequence (speculative verification shape):
     28 layers of partial + combine in one graph, n_q rows per sequence at
@@ -852,7 +885,8 @@ def main():
     ap.add_argument("--kernels-json", default=None)
     ap.add_argument("--write-traffic", default=None)
     ap.add_argument("--mode", choices=["main", "kernels", "ragged", "configs",
-                                       "oracle", "step", "per_head", "rows"],
+                                       "oracle", "step", "per_head", "rows",
+                                       "long"],
                     default="main")
     ap.add_argument("--ragged-batch", type=int, default=32)
     ap.add_argument("--rows", type=int, nargs="*", default=[1, 2, 4, 8],
@@ -892,6 +926,8 @@ def main():
         run_per_head(args)
     elif args.mode == "rows":
         run_rows(args)
+    elif args.mode == "long":
+        run_long(args)
     else:
         run_main(args)
     return 0
