@@ -520,6 +520,47 @@ partial_mfma_kernel(PartialArgs a) {
   // on the kernel's critical path: all of a thread's LDS reads are issued
   // before any of the arithmetic.
   s_run = pair32_sum(pair16_sum(s_run));
+  constexpr int D4 = HD / 4;
+  const size_t pstr = 4 + HD;
+  float *rec0 = a.partials + detail::rec_offset(a, rs, sp, hy * G, HD);
+
+  // A split of at most one tile (short contexts over many splits): only wave
+  // 0 has rows, so it writes the records straight from its registers, with
+  // the same arithmetic as the merge below when waves 1..3 hold the empty
+  // state (weight 0, output 0; the "+ 0" is the merge's fma with a zero
+  // weight, kept for identical signed zeros), and no wave waits at a barrier.
+  if ((uint32_t)lo + kTileRows >= hi32) {
+    if (wave != 0) return;
+    // hi + lo columns first, with every lane of the wave active (the lo
+    // column lanes are the rotation's sources)
+    float4v osum[Geo::DB];
+#pragma unroll
+    for (int i = 0; i < Geo::DB; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) osum[i][k] = add_ror8(oacc[i][k]);
+    if (col >= NC) return;
+    const int r = col / G;
+    if (R > 1 && rs.t + r >= a.n_q) return;
+    const float c = (m_run == neg_inf()) ? 0.0f : fast_exp2(m_run - m_true);
+    float *rec = rec0 + (size_t)(col - r * G) * pstr +
+                 (size_t)r * a.n_head * pstr;
+#pragma unroll
+    for (int i = 0; i < Geo::DB; ++i) {
+      float4 o;
+      o.x = fmaf(c, osum[i][0], 0.0f) + 0.0f;
+      o.y = fmaf(c, osum[i][1], 0.0f) + 0.0f;
+      o.z = fmaf(c, osum[i][2], 0.0f) + 0.0f;
+      o.w = fmaf(c, osum[i][3], 0.0f) + 0.0f;
+      *reinterpret_cast<float4 *>(rec + 4 + 16 * i + 4 * grp) = o;
+    }
+    if (grp == 0)
+      *reinterpret_cast<float4 *>(rec) = make_float4(
+          m_true * detail::kLn2, fmaf(c, s_run, 0.0f) + 0.0f,
+          __builtin_bit_cast(float, (int32_t)rg.lo),
+          __builtin_bit_cast(float, (int32_t)rg.hi));
+    return;
+  }
+
   if (grp == 0 && col < NC) sm_st[wave][col] = make_float4(m_run, m_true, s_run, 0.f);
   wave_lds_fence();  // the slice's last tile reads come first
 #pragma unroll
@@ -532,9 +573,6 @@ partial_mfma_kernel(PartialArgs a) {
           make_float4(o4[0], o4[1], o4[2], o4[3]);
   }
   __syncthreads();
-  constexpr int D4 = HD / 4;
-  const size_t pstr = 4 + HD;
-  float *rec0 = a.partials + detail::rec_offset(a, rs, sp, hy * G, HD);
   for (int idx = tid; idx < NC * D4; idx += kThreads) {
     const int gg = idx / D4;
     const int d4 = idx % D4;
