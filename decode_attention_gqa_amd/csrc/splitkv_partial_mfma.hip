@@ -27,6 +27,13 @@
 // heads' hi parts in columns 0..7 and their lo parts in columns 8..15, so one
 // MFMA computes both halves and a DPP row rotation by 8 adds them.
 //
+// Start of a workgroup: wave 0 issues the query loads before the live length
+// is read (they do not depend on it), every wave then issues its first
+// tile's loads, wave 0 converts the queries into the MFMA operand once and
+// the waves read it from LDS after one barrier. End: the four waves' states
+// are merged through LDS into one record per query head; a split of at most
+// one tile has rows only in wave 0, which writes the records itself.
+//
 // Data flow of one wave over a tile of 16 rows (a workgroup's waves take
 // interleaved tiles):
 //   loads: K and V with 16-byte loads that each cover whole 2*hd-byte rows
