@@ -43,9 +43,9 @@ struct SplitRange {
 // length the host checks block_len * n_splits <= INT_MAX, and otherwise
 // (sp + 1) * chunk < nkv + n_splits. (This runs between the live-length load
 // and the first K/V load of every workgroup, so it avoids 64-bit division.)
-__device__ __forceinline__ SplitRange split_range(const PartialArgs &a,
-                                                  int sp, int b) {
-  const int p = a.positions[b];
+// p = positions[b], read by the caller (so that it can issue the read early).
+__device__ __forceinline__ SplitRange split_range_at(const PartialArgs &a,
+                                                     int sp, int p) {
   const uint32_t mc = (uint32_t)a.max_ctx;
   const uint32_t nkv = p < 0 ? 0u : ((uint32_t)p >= mc ? mc : (uint32_t)p + 1u);
   const uint32_t ns = (uint32_t)a.n_splits;
@@ -57,6 +57,10 @@ __device__ __forceinline__ SplitRange split_range(const PartialArgs &a,
   r.lo = lo;
   r.hi = h < nkv ? h : nkv;
   return r;
+}
+__device__ __forceinline__ SplitRange split_range(const PartialArgs &a,
+                                                  int sp, int b) {
+  return split_range_at(a, sp, a.positions[b]);
 }
 
 // The (sequence, query row) a partial workgroup serves: blockIdx.z =
@@ -82,12 +86,17 @@ __device__ __forceinline__ RowSel row_sel(const PartialArgs &a) {
   return r;
 }
 
-// End of query row t of sequence b within the split [lo, hi).
-__device__ __forceinline__ long long row_end_at(const PartialArgs &a, int b,
-                                                int t, long long hi) {
-  long long n = (long long)a.positions[b] + 1 - (a.n_q - 1 - t);
+// End of query row t of sequence b within the split [lo, hi); p =
+// positions[b].
+__device__ __forceinline__ long long row_end_pos(const PartialArgs &a, int p,
+                                                 int t, long long hi) {
+  long long n = (long long)p + 1 - (a.n_q - 1 - t);
   n = n < 0 ? 0 : (n > a.max_ctx ? a.max_ctx : n);
   return n < hi ? n : hi;
+}
+__device__ __forceinline__ long long row_end_at(const PartialArgs &a, int b,
+                                                int t, long long hi) {
+  return row_end_pos(a, a.positions[b], t, hi);
 }
 __device__ __forceinline__ long long row_end(const PartialArgs &a,
                                              const RowSel &rs, long long hi) {

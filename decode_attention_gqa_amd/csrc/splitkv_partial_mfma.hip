@@ -395,6 +395,10 @@ partial_mfma_kernel(PartialArgs a) {
     col_g = col_valid ? gq - r_c * G : 0;
   }
 
+  // a1: the live length's read is issued first; its latency (it queues
+  // behind other workgroups' K/V loads) overlaps the query loads below.
+  const int pos_b = a.positions[b];
+
   // a3: the queries do not depend on the live length, so wave 0 issues their
   // loads before the live length is read (the other waves take the converted
   // operand from LDS, below). Lane (grp, col) loads dims 32*ks + 8*grp .. +7
@@ -411,18 +415,18 @@ partial_mfma_kernel(PartialArgs a) {
     }
   }
 
-  const detail::SplitRange rg = detail::split_range(a, sp, b);
+  const detail::SplitRange rg = detail::split_range_at(a, sp, pos_b);
   const long long lo = rg.lo;
   long long hi, mask_from, col_end;
   if constexpr (R == 1) {
-    hi = detail::row_end(a, rs, rg.hi);
+    hi = a.n_q == 1 ? rg.hi : detail::row_end_pos(a, pos_b, rs.t, rg.hi);
     mask_from = hi;
     col_end = hi;
   } else {
     const int t_last = min(rs.t + R - 1, a.n_q - 1);
-    hi = detail::row_end_at(a, b, t_last, rg.hi);
-    mask_from = detail::row_end_at(a, b, rs.t, rg.hi);
-    col_end = col_valid ? detail::row_end_at(a, b, col_t, rg.hi) : hi;
+    hi = detail::row_end_pos(a, pos_b, t_last, rg.hi);
+    mask_from = detail::row_end_pos(a, pos_b, rs.t, rg.hi);
+    col_end = col_valid ? detail::row_end_pos(a, pos_b, col_t, rg.hi) : hi;
   }
 
   // This (sequence, KV head) slice of the caches: row r at byte r * row_bytes.
