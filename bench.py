@@ -586,8 +586,10 @@ def run_oracle(args):
 
 def run_step(args):
     """A whole decode step per layer: KV-cache append of the new row, then
-    partial + combine, 28 layers in one graph, at several live lengths; plus
-    the append kernel alone (graph of launches, HIP events)."""
+    partial + combine, 28 layers in one graph, at several live lengths; the
+    same step with the append folded into the partial kernel
+    (splitkv_decode_step); plus the append kernel alone (graph of launches,
+    HIP events)."""
     import torch
 
     import decode_attention_gqa_amd as skv
@@ -623,17 +625,35 @@ def run_step(args):
     with torch.cuda.graph(graph):
         full()
     torch.cuda.synchronize()
+    # the same step with the append folded into the partial kernel
+    def folded():
+        for l in range(lay.L):
+            skv.decode_step(lay.q[l], kn[l], vn[l], lay.k[l], lay.v[l], lay.pos,
+                            lay.part[l], lay.out[l], S, blk, lay.scale)
+
+    with torch.cuda.stream(side):
+        folded()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph_f = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph_f):
+        folded()
+    torch.cuda.synchronize()
     a_mean, _ = time_kernel(torch, append, lay.L, args.kernel_reps)
     row_bytes = 4 * 128 * (4 + 4 + 2 + 2)   # K,V fp32 read + fp16 written
     for nkv in args.points:
         lay.set_nkv(nkv)
         per, _, _ = time_replays(torch, graph, args.warmup, args.steps)
         med = statistics.median(per)
+        per_f, _, _ = time_replays(torch, graph_f, args.warmup, args.steps)
+        med_f = statistics.median(per_f)
         kv = synth.kv_bytes(4, 128, nkv) * lay.L
         print(json.dumps({"decode_step": True, "nkv": nkv, "n_splits": S,
                           "layers": lay.L,
                           "us_per_layer": round(med * 1e3 / lay.L, 3),
                           "kv_gbps": round(kv / (med * 1e-3) / 1e9, 1),
+                          "folded_us_per_layer": round(med_f * 1e3 / lay.L, 3),
+                          "folded_kv_gbps": round(kv / (med_f * 1e-3) / 1e9, 1),
                           "append_avg_us": round(a_mean * 1e3, 3),
                           "append_bytes": row_bytes}), flush=True)
 

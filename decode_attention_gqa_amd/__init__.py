@@ -60,6 +60,8 @@ SIGNATURES = {
                                  _i, _i, _i, _f, _vp]),
     "splitkv_append_kv": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
                                _vp]),
+    "splitkv_decode_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i,
+                                 _i, _i, _i, _i, _i, _i, _f, _vp]),
     "splitkv_probe_read": (_i, [_vp, _sz, _vp, _i, _vp]),
     "splitkv_probe_copy": (_i, [_vp, _vp, _sz, _i, _vp]),
 }
@@ -315,6 +317,31 @@ def append_kv(k_new, v_new, k_cache, v_cache, positions, stream=None):
         k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
         v_cache.data_ptr(), positions.data_ptr(), B, n_rows, nkvh, hd, max_ctx,
         _stream_ptr(stream)), "splitkv_append_kv")
+
+
+def decode_step(q, k_new, v_new, k_cache, v_cache, positions, partials, out,
+                n_splits: int, block_len: int = 0, scale: float | None = None,
+                stream=None):
+    """One decode step: the new fp32 rows [B][1][n_kv_head][hd] go into the
+    fp16 caches at positions[b], then attention over rows [0, positions[b]]
+    (the append folded into the partial kernel for hd 64/128/256)."""
+    torch = _torch()
+    B, nh, nkvh, hd, max_ctx = _shapes(q, k_cache, v_cache, positions)
+    _partials_ok(partials, B, nh, hd, n_splits)
+    _need(out, (torch.float32,), "out")
+    if tuple(out.shape) != (B, nh, hd):
+        raise ValueError("out must be [B][n_head][hd]")
+    _need(k_new, (torch.float32,), "k_new")
+    _need(v_new, (torch.float32,), "v_new")
+    if (tuple(k_new.shape) != (B, 1, nkvh, hd) or
+            tuple(v_new.shape) != (B, 1, nkvh, hd)):
+        raise ValueError("k_new and v_new must be [B][1][n_kv_head][hd]")
+    scale = 1.0 / math.sqrt(hd) if scale is None else float(scale)
+    _check(load().splitkv_decode_step(
+        q.data_ptr(), k_new.data_ptr(), v_new.data_ptr(), k_cache.data_ptr(),
+        v_cache.data_ptr(), positions.data_ptr(), partials.data_ptr(),
+        out.data_ptr(), B, nh, nkvh, hd, max_ctx, n_splits, block_len, scale,
+        _stream_ptr(stream)), "splitkv_decode_step")
 
 
 def probe_read(buf, sink, grid: int, stream=None):

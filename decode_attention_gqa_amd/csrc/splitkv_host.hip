@@ -83,7 +83,9 @@ int do_partial(const float *q, const uint16_t *k, const uint16_t *v,
                const int32_t *positions, float *partials, int batch,
                int n_head, int n_kv_head, int head_dim, int max_ctx,
                int n_splits, int block_len, float scale, void *stream,
-               bool per_head = false, int n_q = 1) {
+               bool per_head = false, int n_q = 1,
+               const float *k_new = nullptr, const float *v_new = nullptr,
+               uint16_t *k_app = nullptr, uint16_t *v_app = nullptr) {
   splitkv::PartialArgs a;
   a.q = q;
   a.k = k;
@@ -98,6 +100,10 @@ int do_partial(const float *q, const uint16_t *k, const uint16_t *v,
   a.scale_log2 = (float)((double)scale * kLog2e);
   a.kv_group = n_head / n_kv_head;
   a.n_q = n_q;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.k_app = k_app;
+  a.v_app = v_app;
   const hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e =
       per_head ? splitkv::launch_partial_per_head(head_dim, a, batch, s)
@@ -323,6 +329,37 @@ int splitkv_append_kv(const float *k_new, const float *v_new,
                  hipSuccess
              ? SPLITKV_OK
              : SPLITKV_ELAUNCH;
+}
+
+int splitkv_decode_step(const float *q, const float *k_new, const float *v_new,
+                        uint16_t *k_cache, uint16_t *v_cache,
+                        const int32_t *positions, float *partials, float *out,
+                        int batch, int n_head, int n_kv_head, int head_dim,
+                        int max_ctx, int n_splits, int block_len, float scale,
+                        void *stream) {
+  int st = check_partial(q, k_cache, v_cache, positions, partials, batch,
+                         n_head, n_kv_head, head_dim, max_ctx, n_splits,
+                         block_len, scale);
+  if (st != SPLITKV_OK) return st;
+  st = check_combine(partials, out, batch, n_head, head_dim, n_splits);
+  if (st != SPLITKV_OK) return st;
+  if (!k_new || !v_new) return SPLITKV_EINVAL;
+  if (!aligned(k_new, 16) || !aligned(v_new, 16)) return SPLITKV_EALIGN;
+  if (head_dim >= 64) {
+    // matrix-core kernel: the append is folded into the partial kernel
+    st = do_partial(q, k_cache, v_cache, positions, partials, batch, n_head,
+                    n_kv_head, head_dim, max_ctx, n_splits, block_len, scale,
+                    stream, false, 1, k_new, v_new, k_cache, v_cache);
+  } else {
+    st = splitkv_append_kv(k_new, v_new, k_cache, v_cache, positions, batch, 1,
+                           n_kv_head, head_dim, max_ctx, stream);
+    if (st != SPLITKV_OK) return st;
+    st = do_partial(q, k_cache, v_cache, positions, partials, batch, n_head,
+                    n_kv_head, head_dim, max_ctx, n_splits, block_len, scale,
+                    stream);
+  }
+  if (st != SPLITKV_OK) return st;
+  return do_combine(partials, out, batch, n_head, head_dim, n_splits, stream);
 }
 
 int splitkv_probe_read(const void *buf, size_t bytes, uint32_t *sink,

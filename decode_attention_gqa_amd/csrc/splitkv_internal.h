@@ -24,6 +24,15 @@ struct PartialArgs {
   int kv_group;              // per-query-head form only: n_head / n_kv_head
   int n_q;                   // query rows per sequence (1: one-token decode);
                              // grid z = batch * n_q, one row per workgroup
+  // A decode step with the KV-cache append folded in (matrix-core kernel,
+  // n_q = 1): each sequence's new row (fp32 [B][1][n_kv_head][HD]) is written
+  // at position positions[b] into the caches k_app / v_app (the same buffers
+  // as k / v) by the workgroup whose split holds that position, which also
+  // uses the converted values for that row. All four null otherwise.
+  const float *k_new;
+  const float *v_new;
+  uint16_t *k_app;
+  uint16_t *v_app;
 };
 
 struct CombineArgs {

@@ -206,6 +206,17 @@ constexpr int vmcnt_imm(int n) {
   return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8);
 }
 
+// Eight fp32 values as eight fp16 bit patterns (v_cvt_f16_f32: round to
+// nearest even, overflow to infinity), packed in element order.
+__device__ __forceinline__ uint32_t f16x2_bits(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+}
+__device__ __forceinline__ uint4 f16x8(const float4v &x, const float4v &y) {
+  return make_uint4(f16x2_bits(x[0], x[1]), f16x2_bits(x[2], x[3]),
+                    f16x2_bits(y[0], y[1]), f16x2_bits(y[2], y[3]));
+}
+
 // Issue the loads of the 16-row tile starting at row tb (tb < hi).
 template <int HD>
 __device__ __forceinline__ void load_tile(TileRegs<HD> &t, const uint16_t *kseq,
@@ -338,7 +349,10 @@ __device__ __forceinline__ void compute_tile(
 // R: query rows per workgroup (several query rows per sequence). The MFMA
 // columns then hold (row, head) pairs, column c = r * G + g, so every K/V row
 // is read once for the R rows; with R = 1 each workgroup serves one row.
-template <int HD, int G, bool PER_HEAD = false, int R = 1>
+// FOLD: the decode-step form with the KV-cache append folded in (one query
+// row, grouped); a separate instantiation, so that the plain forms keep
+// their register count.
+template <int HD, int G, bool PER_HEAD = false, int R = 1, bool FOLD = false>
 __global__ __launch_bounds__(kThreads, 2) void
 partial_mfma_kernel(PartialArgs a) {
   using Geo = MGeo<HD>;
@@ -346,6 +360,7 @@ partial_mfma_kernel(PartialArgs a) {
   constexpr int NC = G * R;                          // MFMA columns in use
   static_assert(G >= 1 && G <= 8 && NC <= 8, "group x rows");
   static_assert(!PER_HEAD || (G == 1 && R == 1), "per-head form: one head");
+  static_assert(!FOLD || (!PER_HEAD && R == 1), "folded append: one row");
   const int sp = blockIdx.x;
   const int hy = blockIdx.y;                         // first query head / G
   const int hk = PER_HEAD ? hy / a.kv_group : hy;    // KV head
@@ -443,6 +458,53 @@ partial_mfma_kernel(PartialArgs a) {
   uint32_t t0 = (uint32_t)lo + (uint32_t)(wave * kTileRows);
   if (lo >= hi) t0 = hi32;  // idle split
 
+  // Folded append (a decode step with one query row): this sequence's new
+  // row for this KV head goes to position pos_b. The wave whose tile holds
+  // that position issues the new row's loads now; on reaching the tile it
+  // writes the row into the caches and uses the converted values in place of
+  // the ones it loaded (the cache still held that row's previous contents).
+  uint32_t app_tb = 0xFFFFFFFFu;    // start of the tile holding the new row
+  float4v knew[2], vnew[2];         // this lane's 8 dims of it, fp32
+  if constexpr (FOLD) {
+    if (a.k_new != nullptr && pos_b >= 0 && pos_b < a.max_ctx &&
+        (long long)pos_b >= lo && (long long)pos_b < hi) {
+      const uint32_t j = ((uint32_t)pos_b - (uint32_t)lo) / kTileRows;
+      if ((int)(j % kWaves) == wave) {
+        app_tb = (uint32_t)lo + j * kTileRows;
+        const size_t src =
+            ((size_t)b * a.n_kv_head + hk) * HD + 8 * (lane % Geo::LPR);
+        knew[0] = *reinterpret_cast<const float4v *>(a.k_new + src);
+        knew[1] = *reinterpret_cast<const float4v *>(a.k_new + src + 4);
+        vnew[0] = *reinterpret_cast<const float4v *>(a.v_new + src);
+        vnew[1] = *reinterpret_cast<const float4v *>(a.v_new + src + 4);
+      }
+    }
+  }
+  auto put_new_row = [&](TileRegs<HD> &t) {
+    const uint32_t r = (uint32_t)pos_b - app_tb;       // row in the tile
+    const bool mine = (uint32_t)(lane / Geo::LPR) == r % Geo::RPI;
+    // Pinned here: hoisted to where the loads are issued, the conversion
+    // would make the wave wait for the new row before its first tile's loads.
+    float4v k0 = knew[0], k1 = knew[1], v0 = vnew[0], v1 = vnew[1];
+    asm volatile("" : "+v"(k0), "+v"(k1), "+v"(v0), "+v"(v1));
+    const uint4 kh = f16x8(k0, k1);
+    const uint4 vh = f16x8(v0, v1);
+#pragma unroll
+    for (int i = 0; i < Geo::NL; ++i) {
+      if (i == (int)(r / Geo::RPI) && mine) {
+        t.k[i] = kh;
+        t.v[i] = vh;
+      }
+    }
+    if (mine) {
+      const size_t dst = ((size_t)b * a.max_ctx + (size_t)pos_b) *
+                             (size_t)a.n_kv_head * HD +
+                         (size_t)hk * HD + 8 * (lane % Geo::LPR);
+      *reinterpret_cast<uint4 *>(a.k_app + dst) = kh;
+      *reinterpret_cast<uint4 *>(a.v_app + dst) = vh;
+    }
+  };
+
   float4v oacc[Geo::DB];
 #pragma unroll
   for (int i = 0; i < Geo::DB; ++i) oacc[i] = float4v{0.f, 0.f, 0.f, 0.f};
@@ -450,8 +512,6 @@ partial_mfma_kernel(PartialArgs a) {
   float m_true = neg_inf();  // exact running max
   float s_run = 0.0f;
 
-  // A wave whose first tile starts at or past hi has no rows: it keeps the
-  // empty state (-inf, 0, 0) and issues no K/V loads at all.
   // B operand of S = K·Q'ᵀ, the same in every wave: column col holds (row,
   // head) col % 8, hi part in columns 0..7 and lo part in 8..15 (zero for
   // unused columns), dims 32*ks + 8*grp + e, pre-scaled to base-2 units.
@@ -488,6 +548,8 @@ partial_mfma_kernel(PartialArgs a) {
   // query loads, and an idle wave 0 drains its unused ones; explicit waits
   // tell the counters so (with 2 * NL tile loads issued the first returns at
   // once). The barrier orders LDS only: the operand is the one thing shared.
+  // A wave whose first tile starts at or past hi has no rows: it keeps the
+  // empty state (-inf, 0, 0) and issues no K/V loads at all.
   const bool busy = t0 < hi32;
   if (busy) {
     TileRegs<HD> tr;
@@ -511,6 +573,9 @@ partial_mfma_kernel(PartialArgs a) {
     // because deeper memory queues serve the workgroups dispatched last later
     // still.
     while (true) {
+      if constexpr (FOLD) {
+        if (t0 == app_tb) put_new_row(tr);
+      }
       compute_tile<HD, (R > 1)>(tr, slice, t0, mask32, lim32, qf, oacc, m_run,
                                 m_true, s_run, col, grp, lane, hi_col);
       t0 += step;
@@ -624,9 +689,14 @@ partial_mfma_kernel(PartialArgs a) {
 
 template <int HD, int G>
 hipError_t launch_one(const PartialArgs &a, int batch, hipStream_t stream) {
-  hipLaunchKernelGGL((partial_mfma_kernel<HD, G>),
-                     dim3(a.n_splits, a.n_kv_head, batch * a.n_q),
-                     dim3(kThreads), 0, stream, a);
+  if (a.k_new != nullptr)
+    hipLaunchKernelGGL((partial_mfma_kernel<HD, G, false, 1, true>),
+                       dim3(a.n_splits, a.n_kv_head, batch), dim3(kThreads),
+                       0, stream, a);
+  else
+    hipLaunchKernelGGL((partial_mfma_kernel<HD, G>),
+                       dim3(a.n_splits, a.n_kv_head, batch * a.n_q),
+                       dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }
 

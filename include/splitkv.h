@@ -213,6 +213,31 @@ int splitkv_append_kv(const float *k_new, const float *v_new,
                       const int32_t *positions, int batch, int n_rows,
                       int n_kv_head, int head_dim, int max_ctx, void *stream);
 
+/* One decode step of one layer: splitkv_append_kv with n_rows = 1, then
+ * splitkv_decode_attn (dotLLM issue #199, comment 1, section 1: the new K/V
+ * row goes into the FP16 cache, then attention reads the cache). For
+ * head_dim 64/128/256 the append is folded into the partial kernel: the
+ * workgroup whose split holds position positions[b] converts sequence b's
+ * new row, writes it into the caches and uses the converted values for that
+ * row, so the step takes two launches instead of three. For head_dim
+ * 8/16/32 the append kernel runs first. Either way the caches afterwards and
+ * `out` are bit for bit those of the two separate calls.
+ *   k_new, v_new      device, fp32 [batch][1][n_kv_head][head_dim], 16-byte
+ *                     aligned; read only; must not overlap the caches.
+ *   k_cache, v_cache  device, fp16 bits [batch][max_ctx][n_kv_head][head_dim],
+ *                     16-byte aligned; row positions[b] is written for every
+ *                     b with 0 <= positions[b] < max_ctx (nothing else is
+ *                     written), then rows [0, nkv_b) are read.
+ *   the other arguments as for splitkv_decode_attn.
+ * Errors: as splitkv_decode_attn, plus SPLITKV_EINVAL for a null k_new or
+ * v_new and SPLITKV_EALIGN when either is not 16-byte aligned. */
+int splitkv_decode_step(const float *q, const float *k_new, const float *v_new,
+                        uint16_t *k_cache, uint16_t *v_cache,
+                        const int32_t *positions, float *partials, float *out,
+                        int batch, int n_head, int n_kv_head, int head_dim,
+                        int max_ctx, int n_splits, int block_len, float scale,
+                        void *stream);
+
 #ifdef __cplusplus
 }
 #endif

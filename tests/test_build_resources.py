@@ -38,15 +38,18 @@ def _kernels(text):
 def test_every_kernel_without_scratch_or_spills():
     ks = _kernels(_report())
     partial = [k for k in ks if "partial_" in k]
-    # template arguments <HD, G, PER_HEAD, R>: the per-head form has
-    # PER_HEAD = true, R = 1
-    per_head = [k for k in partial if re.search(r"ELb1ELi1EE", k)]
-    rows = [k for k in partial if re.search(r"ELb0ELi[248]EE", k)]
+    # template arguments <HD, G, PER_HEAD, R, FOLD>: the per-head form has
+    # PER_HEAD = true, R = 1; the decode-step form FOLD = true
+    per_head = [k for k in partial if re.search(r"ELb1ELi1ELb0EE", k)]
+    rows = [k for k in partial if re.search(r"ELb0ELi[248]ELb0EE", k)]
+    fold = [k for k in partial if re.search(r"ELb0ELi1ELb1EE", k)]
     # 6 head dims x 8 group sizes, the 3 per-query-head forms (hd 64/128/256),
-    # 7 (group, rows) forms for several query rows x 3 head dims, plus
-    # combine, append and probe kernels
-    assert len(partial) == 72 and len(per_head) == 3 and len(rows) == 21, \
-        (len(partial), len(per_head), len(rows))
+    # 7 (group, rows) forms for several query rows x 3 head dims, the
+    # decode-step form for 8 group sizes x 3 head dims, plus combine, append
+    # and probe kernels
+    assert (len(partial) == 96 and len(per_head) == 3 and len(rows) == 21
+            and len(fold) == 24), (len(partial), len(per_head), len(rows),
+                                   len(fold))
     assert any("combine_kernel" in k for k in ks)
     for name, f in ks.items():
         assert f.get("ScratchSize", 0) == 0, (name, f)
@@ -57,7 +60,7 @@ def test_every_kernel_without_scratch_or_spills():
 @pytest.mark.parametrize("hd,g,occ", [(128, 7, 4), (64, 8, 7), (256, 8, 2)])
 def test_matrix_core_kernel_occupancy(hd, g, occ):
     ks = _kernels(_report())
-    name = [k for k in ks if f"partial_mfma_kernelILi{hd}ELi{g}E" in k]
+    name = [k for k in ks if f"partial_mfma_kernelILi{hd}ELi{g}ELb0ELi1ELb0EE" in k]
     assert name, (hd, g)
     f = ks[name[0]]
     assert f.get("Occupancy", 0) >= occ, f
@@ -72,17 +75,24 @@ def test_workgroups_per_cu_matches_compiler_report(splitkv_lib_path):
     seen = 0
     for name, f in ks.items():
         m = re.search(r"partial_(?:mfma|valu)_kernelILi(\d+)ELi(\d+)E", name)
-        if not m or re.search(r"ELb1ELi1EE|ELb0ELi[248]EE", name):
-            continue                  # the per-head and several-row forms aside
+        if not m or re.search(r"ELb1ELi1ELb0EE|ELb0ELi[248]ELb0EE|ELb1EE", name):
+            continue   # the per-head, several-row and decode-step forms aside
         hd, g = int(m.group(1)), int(m.group(2))
         assert skv.workgroups_per_cu(hd, g) == f["Occupancy"], (hd, g, f)
         seen += 1
     assert seen == 48
     # the several-row forms fit as many workgroups per CU as the one-row form
     for name, f in ks.items():
-        m = re.search(r"partial_mfma_kernelILi(\d+)ELi(\d+)ELb0ELi[248]EE", name)
+        m = re.search(r"partial_mfma_kernelILi(\d+)ELi(\d+)ELb0ELi[248]ELb0EE", name)
         if m:
             hd, g = int(m.group(1)), int(m.group(2))
             assert skv.workgroups_per_cu(hd, g) == f["Occupancy"], (name, f)
+    # the decode-step form keeps one round of the heuristic's workgroups
+    # resident (at most 256 / hd per compute unit for one sequence)
+    for name, f in ks.items():
+        m = re.search(r"partial_mfma_kernelILi(\d+)ELi(\d+)ELb0ELi1ELb1EE", name)
+        if m:
+            hd = int(m.group(1))
+            assert f["Occupancy"] >= 256 // hd, (name, f)
     assert skv.workgroups_per_cu(96, 4) == 0
     assert skv.workgroups_per_cu(128, 9) == 0
