@@ -749,8 +749,8 @@ def run_rows(args):
     """Several query rows per sequence (speculative verification shape):
     28 layers of partial + combine in one graph, n_q rows per sequence at
     several live lengths, for the head layout given by --rows-heads (query
-    heads, KV heads; hd128). The split count comes from the heuristic with
-    batch * n_q workgroup rows."""
+    heads, KV heads; hd128). The split count comes from the heuristic for
+    several rows (splitkv_pick_splits_rows)."""
     import torch
 
     import decode_attention_gqa_amd as skv
@@ -766,7 +766,7 @@ def run_rows(args):
     g = torch.Generator(device=dev)
     g.manual_seed(4)
     for n_q in args.rows:
-        S, blk = skv.pick_splits(n_q, nh, nkvh, 128, max_ctx, cu)
+        S, blk = skv.pick_splits_rows(1, n_q, nh, nkvh, 128, max_ctx, cu)
         qs = [torch.randn((1, n_q, nh, 128), generator=g, device=dev)
               for _ in range(base.L)]
         parts = [torch.empty(skv.partials_bytes(1, n_q * nh, 128, S) // 4,

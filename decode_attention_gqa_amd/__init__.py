@@ -47,6 +47,8 @@ SIGNATURES = {
     "splitkv_workgroups_per_cu": (_i, [_i, _i]),
     "splitkv_pick_splits": (_i, [_i, _i, _i, _i, _i, _i,
                                  ctypes.POINTER(_i), ctypes.POINTER(_i)]),
+    "splitkv_pick_splits_rows": (_i, [_i, _i, _i, _i, _i, _i, _i,
+                                      ctypes.POINTER(_i), ctypes.POINTER(_i)]),
     "splitkv_partial": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _i,
                              _i, _f, _vp]),
     "splitkv_partial_rows": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
@@ -129,6 +131,19 @@ def pick_splits(batch: int, n_head: int, n_kv_head: int, head_dim: int,
     _check(load().splitkv_pick_splits(batch, n_head, n_kv_head, head_dim,
                                       max_ctx, cu_count, ctypes.byref(s),
                                       ctypes.byref(blk)), "pick_splits")
+    return s.value, blk.value
+
+
+def pick_splits_rows(batch: int, n_q: int, n_head: int, n_kv_head: int,
+                     head_dim: int, max_ctx: int,
+                     cu_count: int) -> tuple[int, int]:
+    """(n_splits, block_len) for n_q query rows per sequence."""
+    s = _i(0)
+    blk = _i(0)
+    _check(load().splitkv_pick_splits_rows(batch, n_q, n_head, n_kv_head,
+                                           head_dim, max_ctx, cu_count,
+                                           ctypes.byref(s), ctypes.byref(blk)),
+           "pick_splits_rows")
     return s.value, blk.value
 
 

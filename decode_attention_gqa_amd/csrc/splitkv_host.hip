@@ -169,12 +169,26 @@ int splitkv_workgroups_per_cu(int head_dim, int group) {
 int splitkv_pick_splits(int batch, int n_head, int n_kv_head, int head_dim,
                         int max_ctx, int cu_count, int *n_splits,
                         int *block_len) {
-  if (!n_splits || !block_len || cu_count < 1) return SPLITKV_EINVAL;
+  return splitkv_pick_splits_rows(batch, 1, n_head, n_kv_head, head_dim,
+                                  max_ctx, cu_count, n_splits, block_len);
+}
+
+int splitkv_pick_splits_rows(int batch, int n_q, int n_head, int n_kv_head,
+                             int head_dim, int max_ctx, int cu_count,
+                             int *n_splits, int *block_len) {
+  if (!n_splits || !block_len || cu_count < 1 || n_q < 1) return SPLITKV_EINVAL;
   const int st =
       check_shape(batch, n_head, n_kv_head, head_dim, max_ctx, 1, 0);
   if (st != SPLITKV_OK) return st;
   const int group = n_head / n_kv_head;
-  const long long units = (long long)batch * n_kv_head;
+  // Workgroups per split: one per (KV head, sequence, block of rows that
+  // share a workgroup's MFMA columns). The rows of one sequence have about
+  // the same length, so only several sequences call for the balancing rule.
+  const int rows = head_dim >= 64
+                       ? splitkv::rows_per_workgroup(head_dim, group, n_q)
+                       : 1;
+  const long long units =
+      (long long)batch * ((n_q + rows - 1) / rows) * n_kv_head;
   long long wpc = splitkv_workgroups_per_cu(head_dim, group);
   // The matrix-core kernel (head_dim >= 64): at most 256 / head_dim resident
   // workgroups per compute unit (2 at hd 128). Each wave keeps one 16-row

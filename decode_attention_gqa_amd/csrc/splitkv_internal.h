@@ -56,6 +56,10 @@ struct AppendArgs {
 
 // Launchers: enqueue one kernel on `stream` and return hipGetLastError().
 // The host code validates every argument before calling them.
+// Query rows that share one matrix-core partial workgroup for n_q rows per
+// sequence (1 for the vector-ALU kernel's head sizes is the caller's rule).
+int rows_per_workgroup(int head_dim, int group, int n_q);
+
 hipError_t launch_partial(int head_dim, int group, const PartialArgs &a,
                           int batch, hipStream_t stream);
 hipError_t launch_combine(int head_dim, const CombineArgs &a, int batch,

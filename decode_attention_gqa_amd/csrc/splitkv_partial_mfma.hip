@@ -259,12 +259,16 @@ __device__ __forceinline__ void stage_rows(const uint4 (&x)[MGeo<HD>::NL],
 // have no live row yet (several query rows per workgroup), so -inf maxima are
 // guarded. K is staged first and V only after the softmax, so the V rows
 // (which arrive last) are written while the exponentials run.
-template <int HD, bool SAFE>
+// CB = 1: one 16-column MFMA block, hi parts in columns 0..7 and lo parts in
+// 8..15 (added by a DPP rotation). CB = 2: two blocks of 16 columns, block 0
+// the hi parts and block 1 the lo parts of 16 (row, head) columns (added
+// lane by lane); every product then runs twice.
+template <int HD, bool SAFE, int CB>
 __device__ __forceinline__ void compute_tile(
     const TileRegs<HD> &t, unsigned char *slice, uint32_t tb,
-    uint32_t mask_from, uint32_t lim, const half8 (&qf)[MGeo<HD>::KS],
-    float4v (&oacc)[MGeo<HD>::DB], float &m_run, float &m_true, float &s_run,
-    int col, int grp, int lane, bool hi_col) {
+    uint32_t mask_from, uint32_t lim, const half8 (&qf)[CB][MGeo<HD>::KS],
+    float4v (&oacc)[CB][MGeo<HD>::DB], float &m_run, float &m_true,
+    float &s_run, int col, int grp, int lane, bool hi_col) {
   using Geo = MGeo<HD>;
   unsigned char *vlds = slice + Geo::KTILE;
   // a4: scores S = K · Q'ᵀ, K operands read back from the staged rows.
@@ -274,16 +278,26 @@ __device__ __forceinline__ void compute_tile(
   for (int ks = 0; ks < Geo::KS; ++ks)
     ka[ks] = *reinterpret_cast<const uint4 *>(slice + col * Geo::KSTR +
                                                64 * ks + 16 * grp);
-  float4v sc = float4v{0.f, 0.f, 0.f, 0.f};
+  float4v sc[CB];
 #pragma unroll
-  for (int ks = 0; ks < Geo::KS; ++ks)
-    sc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(ka[ks]), qf[ks], sc,
-                                                0, 0, 0);
+  for (int cb = 0; cb < CB; ++cb) {
+    sc[cb] = float4v{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < Geo::KS; ++ks)
+      sc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(ka[ks]),
+                                                      qf[cb][ks], sc[cb], 0,
+                                                      0, 0);
+  }
   // hi + lo columns; rows at or past the column's end (last tiles only) score
   // -inf.
   float s[4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) s[r] = add_ror8(sc[r]);
+  for (int r = 0; r < 4; ++r) {
+    if constexpr (CB == 1)
+      s[r] = add_ror8(sc[0][r]);
+    else
+      s[r] = sc[0][r] + sc[1][r];
+  }
   if (tb + kTileRows > mask_from) {
 #pragma unroll
     for (int r = 0; r < 4; ++r)
@@ -304,15 +318,20 @@ __device__ __forceinline__ void compute_tile(
   // 0 while m_run is -inf (and with SAFE also while mn still is)
   const float corr = (SAFE && m_run == neg_inf()) ? 0.0f : fast_exp2(m_run - mn);
   const float mref = (SAFE && mn == neg_inf()) ? 0.0f : mn;
-  // p hi or lo parts in this lane's rows: the B operand of O += Vᵀ·P
-  half4 pf;
+  // p hi and lo parts in this lane's rows: the B operands of O += Vᵀ·P
+  half4 pf[CB];
   float pv[4];
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const float p = fast_exp2(s[r] - mref);  // exp2(-inf) = 0
     pv[r] = p;
     const _Float16 h = (_Float16)p;
-    pf[r] = hi_col ? h : (_Float16)(p - (float)h);
+    if constexpr (CB == 1) {
+      pf[0][r] = hi_col ? h : (_Float16)(p - (float)h);
+    } else {
+      pf[0][r] = h;
+      pf[1][r] = (_Float16)(p - (float)h);
+    }
   }
   const float psum = (pv[0] + pv[1]) + (pv[2] + pv[3]);
   // Rescale only when some column's reference moved (else corr is 1 for
@@ -320,7 +339,9 @@ __device__ __forceinline__ void compute_tile(
   if (__any(mn != m_run)) {
     s_run *= corr;
 #pragma unroll
-    for (int b = 0; b < Geo::DB; ++b) oacc[b] *= corr;
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int b = 0; b < Geo::DB; ++b) oacc[cb][b] *= corr;
   }
   s_run += psum;
   m_run = mn;
@@ -336,9 +357,23 @@ __device__ __forceinline__ void compute_tile(
     lds_short4v *a0 = (lds_short4v *)(vlds + (4 * grp + c4) * Geo::VSTR +
                                       (16 * b + 4 * cm) * 2);
     const short4v r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(a0);
-    oacc[b] = __builtin_amdgcn_mfma_f32_16x16x16f16(
-        __builtin_bit_cast(half4, r0), pf, oacc[b], 0, 0, 0);
+#pragma unroll
+    for (int cb = 0; cb < CB; ++cb)
+      oacc[cb][b] = __builtin_amdgcn_mfma_f32_16x16x16f16(
+          __builtin_bit_cast(half4, r0), pf[cb], oacc[cb][b], 0, 0, 0);
   }
+}
+
+// A column's output: hi part + lo part. One block: this lane's column plus
+// the column 8 lanes along (a DPP rotation; every lane of the wave must be
+// active); two blocks: the same lane's entries of both.
+template <int CB, int DB>
+__device__ __forceinline__ float hilo_sum(const float4v (&oacc)[CB][DB], int i,
+                                          int r) {
+  if constexpr (CB == 1)
+    return add_ror8(oacc[0][i][r]);
+  else
+    return oacc[0][i][r] + oacc[1][i][r];
 }
 
 // PER_HEAD = false: one workgroup per (split, KV head, sequence) computes all
@@ -357,8 +392,11 @@ __global__ __launch_bounds__(kThreads, 2) void
 partial_mfma_kernel(PartialArgs a) {
   using Geo = MGeo<HD>;
   constexpr int SLICE = Geo::SLICE;
-  constexpr int NC = G * R;                          // MFMA columns in use
-  static_assert(G >= 1 && G <= 8 && NC <= 8, "group x rows");
+  constexpr int NC = G * R;                          // (row, head) columns
+  // one 16-column block holds 8 columns (hi and lo parts), two hold 16
+  constexpr int CB = NC > 8 ? 2 : 1;
+  static_assert(G >= 1 && G <= 8 && NC <= 16, "group x rows");
+  static_assert(CB == 1 || HD <= 128, "two column blocks: hd 64 and 128");
   static_assert(!PER_HEAD || (G == 1 && R == 1), "per-head form: one head");
   static_assert(!FOLD || (!PER_HEAD && R == 1), "folded append: one row");
   const int sp = blockIdx.x;
@@ -380,23 +418,23 @@ partial_mfma_kernel(PartialArgs a) {
   const int lane = tid & 63;
   const int col = lane & 15;
   const int grp = lane >> 4;
-  const bool hi_col = col < 8;
+  const bool hi_col = col < 8;   // (one column block) hi part of a column
 
   __shared__ __attribute__((aligned(16))) unsigned char sm_v[kWaves * SLICE];
   // each wave's state per column: (reference max, exact max, sum, unused)
   __shared__ float4 sm_st[kWaves][NC];
   // the query operand, converted once per workgroup (lane-major per ks)
-  __shared__ half8 sm_q[Geo::KS][64];
-  // a column's output in the wave's slice: HD floats, padded by 16 floats so
-  // that the columns start in different LDS banks
-  constexpr int OSTR = (HD + 16) * 4;
+  __shared__ half8 sm_q[CB][Geo::KS][64];
+  // a column's output in the wave's slice: HD floats, padded (16 floats, 4
+  // with 16 columns) so that the columns start in different LDS banks
+  constexpr int OSTR = (HD + (NC > 8 ? 4 : 16)) * 4;
   static_assert(NC * OSTR <= SLICE, "output state fits the wave's slice");
 
   // a1 + a2: live length and this split's rows; with several query rows,
   // a row's rows end at min(hi, its own live length). The waves run to the
   // end of the workgroup's last row; masking starts at its first row's end,
   // and each column stops at its own row's end.
-  const int gq = col & 7;                            // this lane's column
+  const int gq = CB == 1 ? (col & 7) : col;          // this lane's column
   bool col_valid;                                    // column maps to a row
   int col_t, col_g;                                  // and its (row, head)
   if constexpr (R == 1) {
@@ -505,9 +543,11 @@ partial_mfma_kernel(PartialArgs a) {
     }
   };
 
-  float4v oacc[Geo::DB];
+  float4v oacc[CB][Geo::DB];
 #pragma unroll
-  for (int i = 0; i < Geo::DB; ++i) oacc[i] = float4v{0.f, 0.f, 0.f, 0.f};
+  for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+    for (int i = 0; i < Geo::DB; ++i) oacc[cb][i] = float4v{0.f, 0.f, 0.f, 0.f};
   float m_run = neg_inf();   // reference max (base-2 units), see compute_tile
   float m_true = neg_inf();  // exact running max
   float s_run = 0.0f;
@@ -524,7 +564,7 @@ partial_mfma_kernel(PartialArgs a) {
       const float x[8] = {qraw[ks][0].x, qraw[ks][0].y, qraw[ks][0].z,
                           qraw[ks][0].w, qraw[ks][1].x, qraw[ks][1].y,
                           qraw[ks][1].z, qraw[ks][1].w};
-      half8 h8;
+      half8 h8, l8;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         // q' = q * scale_log2 as hi + lo: hi = fp16(q'), lo = fp16 of the
@@ -532,10 +572,16 @@ partial_mfma_kernel(PartialArgs a) {
         // rounds the same way whatever the compiler contracts).
         const _Float16 h = (_Float16)(x[e] * a.scale_log2);
         const float lo = __builtin_fmaf(x[e], a.scale_log2, -(float)h);
-        const _Float16 val = hi_col ? h : (_Float16)lo;
-        h8[e] = col_valid ? val : (_Float16)0.0f;
+        if constexpr (CB == 1) {
+          const _Float16 val = hi_col ? h : (_Float16)lo;
+          h8[e] = col_valid ? val : (_Float16)0.0f;
+        } else {
+          h8[e] = col_valid ? h : (_Float16)0.0f;
+          l8[e] = col_valid ? (_Float16)lo : (_Float16)0.0f;
+        }
       }
-      sm_q[ks][lane] = h8;
+      sm_q[0][ks][lane] = h8;
+      if constexpr (CB == 2) sm_q[1][ks][lane] = l8;
     }
   };
   // Wave 0 has the split's first tile, so when it has no rows no wave has and
@@ -559,9 +605,11 @@ partial_mfma_kernel(PartialArgs a) {
     else
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * Geo::NL));
     lds_barrier();
-    half8 qf[Geo::KS];
+    half8 qf[CB][Geo::KS];
 #pragma unroll
-    for (int ks = 0; ks < Geo::KS; ++ks) qf[ks] = sm_q[ks][lane];
+    for (int cb = 0; cb < CB; ++cb)
+#pragma unroll
+      for (int ks = 0; ks < Geo::KS; ++ks) qf[cb][ks] = sm_q[cb][ks][lane];
 
     // a4 + a5 over this wave's tiles: compute the landed tile (staged
     // through LDS), then issue the next tile's loads (only tiles with rows:
@@ -576,7 +624,7 @@ partial_mfma_kernel(PartialArgs a) {
       if constexpr (FOLD) {
         if (t0 == app_tb) put_new_row(tr);
       }
-      compute_tile<HD, (R > 1)>(tr, slice, t0, mask32, lim32, qf, oacc, m_run,
+      compute_tile<HD, (R > 1), CB>(tr, slice, t0, mask32, lim32, qf, oacc, m_run,
                                 m_true, s_run, col, grp, lane, hi_col);
       t0 += step;
       if (t0 >= hi32) break;
@@ -613,7 +661,7 @@ partial_mfma_kernel(PartialArgs a) {
 #pragma unroll
     for (int i = 0; i < Geo::DB; ++i)
 #pragma unroll
-      for (int k = 0; k < 4; ++k) osum[i][k] = add_ror8(oacc[i][k]);
+      for (int k = 0; k < 4; ++k) osum[i][k] = hilo_sum<CB>(oacc, i, k);
     if (col >= NC) return;
     const int r = col / G;
     if (R > 1 && rs.t + r >= a.n_q) return;
@@ -643,7 +691,7 @@ partial_mfma_kernel(PartialArgs a) {
   for (int i = 0; i < Geo::DB; ++i) {
     float o4[4];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) o4[r] = add_ror8(oacc[i][r]);
+    for (int r = 0; r < 4; ++r) o4[r] = hilo_sum<CB>(oacc, i, r);
     if (col < NC)
       *reinterpret_cast<float4 *>(slice + col * OSTR + (16 * i + 4 * grp) * 4) =
           make_float4(o4[0], o4[1], o4[2], o4[3]);
@@ -716,17 +764,6 @@ hipError_t launch_hd(int group, const PartialArgs &a, int batch,
   }
 }
 
-// Query rows per workgroup for n_q rows at group size G: as many as the 8
-// MFMA columns hold (G * R <= 8, R in {1, 2, 4, 8}), and no more than the
-// smallest such R that covers n_q.
-int rows_per_workgroup(int group, int n_q) {
-  if (n_q <= 1) return 1;
-  const int cap = group == 1 ? 8 : group == 2 ? 4 : group <= 4 ? 2 : 1;
-  int r = 1;
-  while (r < cap && r < n_q) r *= 2;
-  return r;
-}
-
 template <int HD, int G, int R>
 hipError_t launch_rows(const PartialArgs &a, int batch, hipStream_t stream) {
   const int nrb = (a.n_q + R - 1) / R;
@@ -747,8 +784,19 @@ hipError_t launch_rows_hd(int group, int rows, const PartialArgs &a,
     case 2 * 16 + 4: return launch_rows<HD, 2, 4>(a, batch, stream);
     case 3 * 16 + 2: return launch_rows<HD, 3, 2>(a, batch, stream);
     case 4 * 16 + 2: return launch_rows<HD, 4, 2>(a, batch, stream);
-    default: return hipErrorInvalidValue;
+    default: break;
   }
+  if constexpr (HD <= 128) {
+    // two column blocks
+    switch (group * 16 + rows) {
+      case 5 * 16 + 2: return launch_rows<HD, 5, 2>(a, batch, stream);
+      case 6 * 16 + 2: return launch_rows<HD, 6, 2>(a, batch, stream);
+      case 7 * 16 + 2: return launch_rows<HD, 7, 2>(a, batch, stream);
+      case 8 * 16 + 2: return launch_rows<HD, 8, 2>(a, batch, stream);
+      default: break;
+    }
+  }
+  return hipErrorInvalidValue;
 }
 
 template <int HD>
@@ -760,6 +808,21 @@ hipError_t launch_per_head(const PartialArgs &a, int batch, hipStream_t stream) 
 }
 
 }  // namespace
+
+// Query rows per workgroup for n_q rows at group size G: as many as one
+// 16-column block holds (G * R <= 8, R in {1, 2, 4, 8}), or for G >= 5 two
+// rows in two blocks (hd 64 and 128), and no more than the smallest such R
+// that covers n_q.
+int rows_per_workgroup(int head_dim, int group, int n_q) {
+  if (n_q <= 1) return 1;
+  const int cap = group == 1   ? 8
+                  : group == 2 ? 4
+                  : group <= 4 ? 2
+                  : head_dim <= 128 ? 2 : 1;
+  int r = 1;
+  while (r < cap && r < n_q) r *= 2;
+  return r;
+}
 
 hipError_t launch_partial_per_head(int head_dim, const PartialArgs &a,
                                    int batch, hipStream_t stream) {
@@ -773,7 +836,7 @@ hipError_t launch_partial_per_head(int head_dim, const PartialArgs &a,
 
 hipError_t launch_partial_mfma(int head_dim, int group, const PartialArgs &a,
                                int batch, hipStream_t stream) {
-  const int rows = rows_per_workgroup(group, a.n_q);
+  const int rows = rows_per_workgroup(head_dim, group, a.n_q);
   if (rows > 1) {
     switch (head_dim) {
       case 64: return launch_rows_hd<64>(group, rows, a, batch, stream);

@@ -121,6 +121,14 @@ int splitkv_pick_splits(int batch, int n_head, int n_kv_head, int head_dim,
                         int max_ctx, int cu_count, int *n_splits,
                         int *block_len);
 
+/* The same rule for n_q query rows per sequence (splitkv_partial_rows /
+ * splitkv_decode_attn_rows): counted over the workgroups those launch, where
+ * rows that share a workgroup's MFMA columns count once. n_q = 1 is
+ * splitkv_pick_splits; SPLITKV_EINVAL also for n_q < 1. */
+int splitkv_pick_splits_rows(int batch, int n_q, int n_head, int n_kv_head,
+                             int head_dim, int max_ctx, int cu_count,
+                             int *n_splits, int *block_len);
+
 /* Partial kernel only: writes every record of `partials`. */
 int splitkv_partial(const float *q, const uint16_t *k_cache,
                     const uint16_t *v_cache, const int32_t *positions,
@@ -145,8 +153,12 @@ int splitkv_partial(const float *q, const uint16_t *k_cache,
  *   out       device fp32 [batch][n_q][n_head][head_dim].
  * The splits are cut from the last row's live length positions[b] + 1, as
  * for one row; row t's rows end at min(hi, its live length). One partial
- * workgroup per (split, KV head, sequence, row): grid dim3(n_splits,
- * n_kv_head, batch * n_q). Other arguments and errors as for
+ * workgroup per (split, KV head, sequence, block of rows): a block holds the
+ * rows whose (row, head) pairs fit the workgroup's MFMA columns (G * R <= 8
+ * in one 16-column block, or two rows at G = 5..8 in two blocks for
+ * head_dim 64 and 128; one row otherwise and for head_dim 8/16/32), grid
+ * dim3(n_splits, n_kv_head, batch * ceil(n_q / R)); each K/V row is read once
+ * per block. Other arguments and errors as for
  * splitkv_partial / splitkv_decode_attn, plus SPLITKV_EINVAL when n_q < 1,
  * batch * n_q > 65535 or n_q * n_head > 65535. n_q = 1 is exactly
  * splitkv_partial / splitkv_decode_attn. The combine of these records is

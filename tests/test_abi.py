@@ -90,6 +90,35 @@ def test_pick_splits_properties(lib):
         skv.pick_splits(1, 28, 4, 128, 2048, 0)        # no compute units
 
 
+def test_pick_splits_rows(lib):
+    # one row: the one-row rule
+    for shape in [(1, 28, 4, 128, 2048), (1, 28, 4, 128, 33024),
+                  (1, 16, 2, 256, 8400), (32, 32, 8, 128, 32768),
+                  (1, 4, 2, 64, 256), (1, 4, 2, 8, 1024)]:
+        B, nh, nkvh, hd, T = shape
+        assert (skv.pick_splits_rows(B, 1, nh, nkvh, hd, T, 256) ==
+                skv.pick_splits(*shape, cu_count=256)), shape
+    # Workgroups per split = KV heads x sequences x blocks of rows; rows share
+    # a block when their (row, head) pairs fit the MFMA columns: G = 7 at
+    # hd128 takes 2 rows per block, G = 8 at hd256 one, G = 1 eight, and the
+    # vector-ALU head sizes one. One round of 2 (hd128) / 1 (hd256) resident
+    # workgroups per compute unit on 256 units; hd32 G = 2: 3 per unit,
+    # capped at max_ctx / 32 splits.
+    cases = {(1, 2, 28, 4, 128, 33024): 128,    # 1 block  x 4 heads
+             (1, 4, 28, 4, 128, 33024): 64,     # 2 blocks x 4
+             (1, 8, 28, 4, 128, 33024): 32,     # 4 blocks x 4
+             (1, 3, 28, 4, 128, 33024): 64,     # 2 blocks (last half full)
+             (1, 2, 16, 2, 256, 8400): 64,      # 2 blocks x 2, 1 per unit
+             (1, 8, 8, 8, 128, 32768): 64,      # 1 block  x 8
+             (2, 2, 28, 4, 128, 32768): 64,     # 2 sequences, 8 units
+             (1, 4, 4, 2, 32, 1024): 32}        # 4 rows x 2, capped
+    for (B, n_q, nh, nkvh, hd, T), want in cases.items():
+        assert skv.pick_splits_rows(B, n_q, nh, nkvh, hd, T, 256) == \
+            (want, 0), (B, n_q, nh, nkvh, hd, T)
+    with pytest.raises(skv.SplitKVError):
+        skv.pick_splits_rows(1, 0, 28, 4, 128, 2048, 256)   # no rows
+
+
 # Fake, aligned addresses: every case below must fail validation, so nothing
 # is ever dereferenced or launched. As a second guard these cases only run on
 # hosts without a GPU, where a launch could not reach a device anyway.

@@ -39,9 +39,11 @@ def _run_rows(q, k, v, pos, S, blk, scale):
 def test_rows_parity(hd):
     T = 300
     # G * n_q <= 8 puts several rows in one workgroup's columns (1, 2, 4 or 8
-    # rows, the last block partly filled when n_q is not a multiple); G = 7
-    # keeps one row per workgroup
-    for G, nkvh in ((1, 2), (2, 2), (3, 1), (4, 2), (7, 1)):
+    # rows, the last block partly filled when n_q is not a multiple); G 5..8
+    # put two rows in two column blocks at hd 64 and 128, one row per
+    # workgroup at the other head sizes
+    for G, nkvh in ((1, 2), (2, 2), (3, 1), (4, 2), (5, 1), (6, 1), (7, 1),
+                    (8, 1)):
         nh = G * nkvh
         for n_q in (1, 2, 3, 5, 8):
             # prefill from empty, a chunk mid-cache, at the end, rows before 0
