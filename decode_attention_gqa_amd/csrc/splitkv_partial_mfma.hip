@@ -430,10 +430,8 @@ partial_mfma_kernel(PartialArgs a) {
   constexpr int OSTR = (HD + (NC > 8 ? 4 : 16)) * 4;
   static_assert(NC * OSTR <= SLICE, "output state fits the wave's slice");
 
-  // a1 + a2: live length and this split's rows; with several query rows,
-  // a row's rows end at min(hi, its own live length). The waves run to the
-  // end of the workgroup's last row; masking starts at its first row's end,
-  // and each column stops at its own row's end.
+  // This lane's MFMA column: (row, head) pair c = r * G + g of the
+  // workgroup's rows (column col % 8 in one block, col in two).
   const int gq = CB == 1 ? (col & 7) : col;          // this lane's column
   bool col_valid;                                    // column maps to a row
   int col_t, col_g;                                  // and its (row, head)
@@ -468,6 +466,10 @@ partial_mfma_kernel(PartialArgs a) {
     }
   }
 
+  // a1 + a2: live length and this split's rows; with several query rows,
+  // a row's rows end at min(hi, its own live length). The waves run to the
+  // end of the workgroup's last row; masking starts at its first row's end,
+  // and each column stops at its own row's end.
   const detail::SplitRange rg = detail::split_range_at(a, sp, pos_b);
   const long long lo = rg.lo;
   long long hi, mask_from, col_end;
@@ -552,9 +554,11 @@ partial_mfma_kernel(PartialArgs a) {
   float m_true = neg_inf();  // exact running max
   float s_run = 0.0f;
 
-  // B operand of S = K·Q'ᵀ, the same in every wave: column col holds (row,
-  // head) col % 8, hi part in columns 0..7 and lo part in 8..15 (zero for
-  // unused columns), dims 32*ks + 8*grp + e, pre-scaled to base-2 units.
+  // B operand of S = K·Q'ᵀ, the same in every wave: with one block, column
+  // col holds (row, head) col % 8, hi part in columns 0..7 and lo part in
+  // 8..15; with two, block 0 holds the hi parts and block 1 the lo parts of
+  // columns 0..15 (zero for unused columns); dims 32*ks + 8*grp + e,
+  // pre-scaled to base-2 units.
   // Wave 0 converts it (its query loads come back while the first tile is in
   // flight) and hands it to the other waves through LDS: one query read per
   // workgroup instead of one per wave.
@@ -624,8 +628,9 @@ partial_mfma_kernel(PartialArgs a) {
       if constexpr (FOLD) {
         if (t0 == app_tb) put_new_row(tr);
       }
-      compute_tile<HD, (R > 1), CB>(tr, slice, t0, mask32, lim32, qf, oacc, m_run,
-                                m_true, s_run, col, grp, lane, hi_col);
+      compute_tile<HD, (R > 1), CB>(tr, slice, t0, mask32, lim32, qf, oacc,
+                                    m_run, m_true, s_run, col, grp, lane,
+                                    hi_col);
       t0 += step;
       if (t0 >= hi32) break;
       load_tile<HD>(tr, kseq, vseq, row_bytes, t0, hi32, off);
