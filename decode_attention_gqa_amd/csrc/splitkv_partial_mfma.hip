@@ -794,6 +794,9 @@ hipError_t launch_rows_hd(int group, int rows, const PartialArgs &a,
   if constexpr (HD <= 128) {
     // two column blocks
     switch (group * 16 + rows) {
+      case 2 * 16 + 8: return launch_rows<HD, 2, 8>(a, batch, stream);
+      case 3 * 16 + 4: return launch_rows<HD, 3, 4>(a, batch, stream);
+      case 4 * 16 + 4: return launch_rows<HD, 4, 4>(a, batch, stream);
       case 5 * 16 + 2: return launch_rows<HD, 5, 2>(a, batch, stream);
       case 6 * 16 + 2: return launch_rows<HD, 6, 2>(a, batch, stream);
       case 7 * 16 + 2: return launch_rows<HD, 7, 2>(a, batch, stream);
@@ -814,16 +817,17 @@ hipError_t launch_per_head(const PartialArgs &a, int batch, hipStream_t stream) 
 
 }  // namespace
 
-// Query rows per workgroup for n_q rows at group size G: as many as one
-// 16-column block holds (G * R <= 8, R in {1, 2, 4, 8}), or for G >= 5 two
-// rows in two blocks (hd 64 and 128), and no more than the smallest such R
-// that covers n_q.
+// Query rows per workgroup for n_q rows at group size G, R in {1, 2, 4, 8}:
+// as many as the MFMA columns hold -- one 16-column block holds G * R <= 8
+// (hi and lo parts side by side), two blocks hold G * R <= 16 (hd 64 and
+// 128 only) -- and no more than the smallest such R that covers n_q.
 int rows_per_workgroup(int head_dim, int group, int n_q) {
   if (n_q <= 1) return 1;
+  const bool two = head_dim <= 128;
   const int cap = group == 1   ? 8
-                  : group == 2 ? 4
-                  : group <= 4 ? 2
-                  : head_dim <= 128 ? 2 : 1;
+                  : group == 2 ? (two ? 8 : 4)
+                  : group <= 4 ? (two ? 4 : 2)
+                  : two ? 2 : 1;
   int r = 1;
   while (r < cap && r < n_q) r *= 2;
   return r;

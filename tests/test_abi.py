@@ -99,9 +99,10 @@ def test_pick_splits_rows(lib):
         assert (skv.pick_splits_rows(B, 1, nh, nkvh, hd, T, 256) ==
                 skv.pick_splits(*shape, cu_count=256)), shape
     # Workgroups per split = KV heads x sequences x blocks of rows; rows share
-    # a block when their (row, head) pairs fit the MFMA columns: G = 7 at
-    # hd128 takes 2 rows per block, G = 8 at hd256 one, G = 1 eight, and the
-    # vector-ALU head sizes one. One round of 2 (hd128) / 1 (hd256) resident
+    # a block when their (row, head) pairs fit the MFMA columns (16 at hd 64
+    # and 128, 8 at hd 256): G = 7 at hd128 takes 2 rows per block, G = 4
+    # four, G = 2 eight, G = 8 at hd256 one, G = 1 eight, and the vector-ALU
+    # head sizes one. One round of 2 (hd128) / 1 (hd256) resident
     # workgroups per compute unit on 256 units; hd32 G = 2: 3 per unit,
     # capped at max_ctx / 32 splits.
     cases = {(1, 2, 28, 4, 128, 33024): 128,    # 1 block  x 4 heads
@@ -111,6 +112,10 @@ def test_pick_splits_rows(lib):
              (1, 2, 16, 2, 256, 8400): 64,      # 2 blocks x 2, 1 per unit
              (1, 8, 8, 8, 128, 32768): 64,      # 1 block  x 8
              (2, 2, 28, 4, 128, 32768): 64,     # 2 sequences, 8 units
+             (1, 4, 32, 8, 128, 32768): 64,     # G 4: 4 rows in 1 block x 8
+             (1, 8, 32, 8, 128, 32768): 32,     # 2 blocks x 8
+             (1, 8, 16, 8, 128, 32768): 64,     # G 2: 8 rows in 1 block x 8
+             (1, 4, 32, 8, 256, 32768): 16,     # hd256 G 4: 2 per block, 1/unit
              (1, 4, 4, 2, 32, 1024): 32}        # 4 rows x 2, capped
     for (B, n_q, nh, nkvh, hd, T), want in cases.items():
         assert skv.pick_splits_rows(B, n_q, nh, nkvh, hd, T, 256) == \

@@ -45,10 +45,10 @@ def test_every_kernel_without_scratch_or_spills():
     fold = [k for k in partial if re.search(r"ELb0ELi1ELb1EE", k)]
     # 6 head dims x 8 group sizes, the 3 per-query-head forms (hd 64/128/256),
     # 7 one-block (group, rows) forms for several query rows x 3 head dims
-    # and 4 two-block forms (G 5..8, 2 rows) x hd 64/128, the decode-step
-    # form for 8 group sizes x 3 head dims, plus combine, append and probe
-    # kernels
-    assert (len(partial) == 104 and len(per_head) == 3 and len(rows) == 29
+    # and 7 two-block forms ((2, 8), (3, 4), (4, 4), (5..8, 2)) x hd 64/128,
+    # the decode-step form for 8 group sizes x 3 head dims, plus combine,
+    # append and probe kernels
+    assert (len(partial) == 110 and len(per_head) == 3 and len(rows) == 35
             and len(fold) == 24), (len(partial), len(per_head), len(rows),
                                    len(fold))
     assert any("combine_kernel" in k for k in ks)

@@ -38,10 +38,9 @@ def _run_rows(q, k, v, pos, S, blk, scale):
 @pytest.mark.parametrize("hd", [8, 16, 32, 64, 128, 256])
 def test_rows_parity(hd):
     T = 300
-    # G * n_q <= 8 puts several rows in one workgroup's columns (1, 2, 4 or 8
-    # rows, the last block partly filled when n_q is not a multiple); G 5..8
-    # put two rows in two column blocks at hd 64 and 128, one row per
-    # workgroup at the other head sizes
+    # rows share a workgroup when their (row, head) pairs fit its columns:
+    # G * R <= 8 in one block, G * R <= 16 in two blocks (hd 64 and 128; the
+    # last block partly filled when n_q is not a multiple of R)
     for G, nkvh in ((1, 2), (2, 2), (3, 1), (4, 2), (5, 1), (6, 1), (7, 1),
                     (8, 1)):
         nh = G * nkvh
