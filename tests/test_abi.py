@@ -221,6 +221,32 @@ def test_decode_rejects_bad_out(lib):
     assert _call_decode(lib, a, out=A + 0x5000 + 4) == EALIGN
 
 
+def _call_step(lib, a, kn=A + 0x6000, vn=A + 0x7000, out=A + 0x5000):
+    return lib.splitkv_decode_step(a["q"], kn, vn, a["k"], a["v"], a["pos"],
+                                   a["part"], out, a["B"], a["nh"], a["nkvh"],
+                                   a["hd"], a["T"], a["S"], a["blk"],
+                                   a["scale"], None)
+
+
+@cpu_only
+@pytest.mark.parametrize("what,over,code", BAD_PARTIAL,
+                         ids=[c[0] for c in BAD_PARTIAL])
+def test_decode_step_rejects(lib, what, over, code):
+    """The folded decode step validates like decode_attn, before any
+    launch."""
+    assert _call_step(lib, _partial_args(**over)) == code
+
+
+@cpu_only
+def test_decode_step_rejects_bad_new_rows(lib):
+    a = _partial_args()
+    assert _call_step(lib, a, kn=0) == EINVAL
+    assert _call_step(lib, a, vn=0) == EINVAL
+    assert _call_step(lib, a, kn=A + 0x6000 + 4) == EALIGN
+    assert _call_step(lib, a, vn=A + 0x7000 + 8) == EALIGN
+    assert _call_step(lib, a, out=0) == EINVAL
+
+
 BAD_COMBINE = [
     ("null partials", (0, A + 0x100, 1, 28, 128, 32), EINVAL),
     ("null out", (A, 0, 1, 28, 128, 32), EINVAL),
