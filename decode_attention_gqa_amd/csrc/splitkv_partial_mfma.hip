@@ -653,15 +653,16 @@ partial_mfma_kernel(PartialArgs a) {
   const size_t pstr = 4 + HD;
   float *rec0 = a.partials + detail::rec_offset(a, rs, sp, hy * G, HD);
 
-  // A split of at most one tile (short contexts over many splits): only wave
-  // 0 has rows, so it writes the records straight from its registers, with
-  // the same arithmetic as the merge below when waves 1..3 hold the empty
-  // state (weight 0, output 0; the "+ 0" is the merge's fma with a zero
-  // weight, kept for identical signed zeros), and no wave waits at a barrier.
+  // A split of at most one tile (short contexts over many splits), or an
+  // idle one: only wave 0 can have rows, so it writes the records straight
+  // from its registers, with the same arithmetic as the merge below when
+  // waves 1..3 hold the empty state (weight 0, output 0; the "+ 0" is the
+  // merge's fma with a zero weight, kept for identical signed zeros), and no
+  // wave waits at a barrier.
   if ((uint32_t)lo + kTileRows >= hi32) {
     if (wave != 0) return;
-    // hi + lo columns first, with every lane of the wave active (the lo
-    // column lanes are the rotation's sources)
+    // hi + lo parts first, with every lane of the wave active (with one
+    // column block the lo column lanes are the rotation's sources)
     float4v osum[Geo::DB];
 #pragma unroll
     for (int i = 0; i < Geo::DB; ++i)
