@@ -33,6 +33,7 @@ Usage: python bench.py [--steps K] [--warmup W] [--nkv N] [--layers L]
                                         # grouped vs per-query-head grid
        python bench.py --mode rows      # n_q query rows per sequence (causal)
        python bench.py --mode long      # 28q/4kv hd128 at 16K..128K rows
+       python bench.py --mode batch     # the same shape, 1..8 sequences at 16K/32K
        python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --kernels-json F
                                         # fold two rocprofv3 --pmc runs
 """
@@ -745,6 +746,49 @@ def run_long(args):
               flush=True)
 
 
+def run_batch(args):
+    """The headline shape with several sequences of one length: 28q/4kv
+    hd128, max_ctx 33,024 (or --batch-max-ctx), batch 1..8, one graph of L
+    layers x (partial + combine) per (batch, split count) replayed at
+    --batch-lengths, every layer in its own buffers; the split counts are
+    the heuristic's and the ones given by --extra-splits."""
+    import torch
+
+    import decode_attention_gqa_amd as skv
+    import synth
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    max_ctx = args.batch_max_ctx or synth.CFG3.max_ctx
+    for B in args.batches:
+        sh = synth.Shape(B, 28, 4, 128, max_ctx)
+        log(f"[bench] generating layer data: batch {B}, max_ctx={max_ctx}")
+        case = synth.make_offset_case(3, sh, max_ctx)
+        S_h, _ = skv.pick_splits(B, 28, 4, 128, max_ctx, cu)
+        for S in [S_h] + [x for x in args.extra_splits if x != S_h]:
+            lay = Layers(args.layers, max_ctx, S, 0, sh, case)
+            graph = lay.capture()
+            for nkv in [n for n in args.batch_lengths if n <= max_ctx]:
+                lay.set_nkv(nkv)
+                per, _, _ = time_replays(torch, graph, args.warmup, args.steps)
+                med = statistics.median(per)
+                kv = B * synth.kv_bytes(4, 128, nkv)
+                p_mean, _ = time_kernel(torch, lay.partial, lay.L,
+                                        args.kernel_reps)
+                print(json.dumps({
+                    "batch": B, "nkv": nkv, "max_ctx": max_ctx, "n_splits": S,
+                    "heuristic": S == S_h, "layers": lay.L,
+                    "us_per_layer": round(med * 1e3 / lay.L, 3),
+                    "kv_gbps": round(kv * lay.L / (med * 1e-3) / 1e9, 1),
+                    "pct_hbm_peak": round(100 * kv * lay.L / (med * 1e-3)
+                                          / 1e9 / HBM_PEAK_GBPS, 2),
+                    "partial_avg_us": round(p_mean * 1e3, 3),
+                    "partial_pct_hbm_peak": round(
+                        100 * kv / (p_mean * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)}),
+                    flush=True)
+            del graph, lay
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+
+
 def run_rows(args):
     """Several query rows per sequence (speculative verification shape):
     28 layers of partial + combine in one graph, n_q rows per sequence at
@@ -906,9 +950,15 @@ def main():
     ap.add_argument("--write-traffic", default=None)
     ap.add_argument("--mode", choices=["main", "kernels", "ragged", "configs",
                                        "oracle", "step", "per_head", "rows",
-                                       "long"],
+                                       "long", "batch"],
                     default="main")
     ap.add_argument("--ragged-batch", type=int, default=32)
+    ap.add_argument("--batches", type=int, nargs="*", default=[1, 2, 4, 8],
+                    help="--mode batch: batch sizes")
+    ap.add_argument("--batch-lengths", type=int, nargs="*",
+                    default=[16384, 32768], help="--mode batch: live lengths")
+    ap.add_argument("--batch-max-ctx", type=int, default=0,
+                    help="--mode batch: cache rows per sequence (default 33,024)")
     ap.add_argument("--rows", type=int, nargs="*", default=[1, 2, 4, 8],
                     help="--mode rows: query rows per sequence to time")
     ap.add_argument("--rows-heads", type=int, nargs=2, default=[28, 4],
@@ -948,6 +998,8 @@ def main():
         run_rows(args)
     elif args.mode == "long":
         run_long(args)
+    elif args.mode == "batch":
+        run_batch(args)
     else:
         run_main(args)
     return 0
