@@ -25,12 +25,15 @@
 // fp32; each is split into fp16 hi = fp16(x) and lo = fp16(x - hi), which
 // carry about 22 significant bits together. The 16 MFMA columns hold the G
 // heads' hi parts in columns 0..7 and their lo parts in columns 8..15, so one
-// MFMA computes both halves and a DPP row rotation by 8 adds them.
+// MFMA computes both halves and a DPP row rotation by 8 adds them. (Several
+// query rows of one sequence can share the columns as (row, head) pairs; up
+// to 16 pairs use two column blocks, hi parts in one and lo parts in the
+// other, each product run once per block.)
 //
-// Start of a workgroup: wave 0 issues the query loads before the live length
-// is read (they do not depend on it), every wave then issues its first
-// tile's loads, wave 0 converts the queries into the MFMA operand once and
-// the waves read it from LDS after one barrier. End: the four waves' states
+// Start of a workgroup: the live length is read first and wave 0 issues the
+// query loads while it is in flight (they do not depend on it), every wave
+// then issues its first tile's loads, wave 0 converts the queries into the
+// MFMA operand once and the waves read it from LDS after one barrier. End: the four waves' states
 // are merged through LDS into one record per query head; a split of at most
 // one tile has rows only in wave 0, which writes the records itself.
 //
@@ -451,8 +454,8 @@ partial_mfma_kernel(PartialArgs a) {
   const int pos_b = a.positions[b];
 
   // a3: the queries do not depend on the live length, so wave 0 issues their
-  // loads before the live length is read (the other waves take the converted
-  // operand from LDS, below). Lane (grp, col) loads dims 32*ks + 8*grp .. +7
+  // loads while the live length is in flight (the other waves take the
+  // converted operand from LDS, below). Lane (grp, col) loads dims 32*ks + 8*grp .. +7
   // of column col's (row, head).
   float4 qraw[Geo::KS][2];
   if (wave == 0) {
