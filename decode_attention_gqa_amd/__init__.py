@@ -7,10 +7,11 @@ passes their device pointers and the current HIP stream, and turns a negative
 status into ``SplitKVError``. Every step of the computation runs in the HIP
 kernels. There is no fallback: if the library is missing, every call raises.
 
-Names follow the C ABI: ``decode_attn``, ``partial``, ``partial_per_head``,
-``combine``,
-``append_kv``, ``partials_bytes``, ``pick_splits``, ``workgroups_per_cu``,
-``strerror``.
+Names follow the C ABI (``splitkv_`` dropped): ``decode_attn``,
+``decode_step``, ``decode_attn_rows``, ``partial``, ``partial_rows``,
+``partial_per_head``, ``combine``, ``append_kv``, ``partials_bytes``,
+``pick_splits``, ``pick_splits_rows``, ``workgroups_per_cu``, ``strerror``,
+``probe_read``, ``probe_copy``.
 """
 from __future__ import annotations
 
@@ -20,9 +21,9 @@ import os
 import threading
 
 __all__ = ["SplitKVError", "load", "abi_version", "strerror", "partials_bytes",
-           "pick_splits", "partial", "partial_per_head", "partial_rows",
-           "combine", "decode_attn", "decode_attn_rows", "append_kv",
-           "workgroups_per_cu", "probe_read",
+           "pick_splits", "pick_splits_rows", "partial", "partial_per_head",
+           "partial_rows", "combine", "decode_attn", "decode_attn_rows",
+           "decode_step", "append_kv", "workgroups_per_cu", "probe_read",
            "probe_copy", "LIB_PATH", "SUPPORTED_HEAD_DIMS", "MAX_GROUP"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
@@ -365,8 +366,8 @@ def probe_read(buf, sink, grid: int, stream=None):
     _need(sink, (torch.int32, torch.uint32), "sink")
     if sink.numel() < grid:
         raise ValueError("sink must hold `grid` words")
-    if not buf.is_cuda:
-        raise ValueError("buf must be on a GPU device")
+    if not buf.is_cuda or not buf.is_contiguous():
+        raise ValueError("buf must be a contiguous tensor on a GPU device")
     nbytes = buf.numel() * buf.element_size()
     _check(load().splitkv_probe_read(buf.data_ptr(), nbytes, sink.data_ptr(),
                                      grid, _stream_ptr(stream)), "probe_read")
@@ -374,8 +375,10 @@ def probe_read(buf, sink, grid: int, stream=None):
 
 def probe_copy(src, dst, grid: int, stream=None):
     """Plain 16-byte copy of ``src`` into ``dst`` (same byte size)."""
-    if not (src.is_cuda and dst.is_cuda):
-        raise ValueError("src and dst must be on a GPU device")
+    if not (src.is_cuda and dst.is_cuda and src.is_contiguous() and
+            dst.is_contiguous()):
+        raise ValueError("src and dst must be contiguous tensors on a GPU "
+                         "device")
     nbytes = src.numel() * src.element_size()
     if dst.numel() * dst.element_size() < nbytes:
         raise ValueError("dst is smaller than src")
