@@ -87,6 +87,12 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
                 f"{path} is missing: build it with "
                 "`python -m decode_attention_gqa_amd.build` (no fallback "
                 "implementation exists)")
+        # torch ships its own HIP runtime under the system runtime's soname.
+        # Loaded first, the library would pull in the system runtime and
+        # torch would then load a second one: kernels registered in one,
+        # streams and memory from the other, and every launch fails. With
+        # torch loaded first the library binds to torch's runtime.
+        _torch()
         lib = ctypes.CDLL(path)
         for name, (res, args) in SIGNATURES.items():
             fn = getattr(lib, name)

@@ -328,3 +328,24 @@ def test_rows_reject(lib, what, over, code):
         a["q"], a["k"], a["v"], a["pos"], a["part"], A + 0x5000, a["B"], nq,
         a["nh"], a["nkvh"], a["hd"], a["T"], a["S"], a["blk"], a["scale"],
         None) == code
+
+
+def test_one_hip_runtime_whatever_the_import_order():
+    """Loading the library before torch has been imported must not bring a
+    second HIP runtime into the process (torch ships its own under the same
+    soname): with two, kernels and streams belong to different runtimes and
+    every launch fails."""
+    import subprocess
+    import sys
+    code = (
+        "import decode_attention_gqa_amd as skv\n"
+        "skv.load()\n"
+        "import torch\n"
+        "maps = {l.split()[-1] for l in open('/proc/self/maps')\n"
+        "        if 'libamdhip64' in l}\n"
+        "print(len(maps))\n")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    p = subprocess.run([sys.executable, "-c", code], capture_output=True,
+                       text=True, timeout=300, cwd=root)
+    assert p.returncode == 0, p.stderr
+    assert p.stdout.strip().splitlines()[-1] == "1", p.stdout
