@@ -100,6 +100,7 @@ int do_partial(const float *q, const uint16_t *k, const uint16_t *v,
   a.scale_log2 = (float)((double)scale * kLog2e);
   a.kv_group = n_head / n_kv_head;
   a.n_q = n_q;
+  a.pair_rows = 0;  // chosen by the several-row launcher
   a.k_new = k_new;
   a.v_new = v_new;
   a.k_app = k_app;

@@ -22,8 +22,13 @@ struct PartialArgs {
   int block_len;             // 0: chunk = ceil(nkv / n_splits)
   float scale_log2;          // scale * log2(e): scores are kept in base-2 units
   int kv_group;              // per-query-head form only: n_head / n_kv_head
-  int n_q;                   // query rows per sequence (1: one-token decode);
-                             // grid z = batch * n_q, one row per workgroup
+  int n_q;                   // query rows per sequence (1: one-token decode)
+  // Several-row form with more than one block of rows per sequence: 1 when
+  // the grid is dim3(8 * row blocks, n_splits / 8, n_kv_head * batch), which
+  // puts the row blocks of one (split, KV head, sequence) 8 apart in the
+  // dispatch order; 0 for the plain grid dim3(n_splits, n_kv_head, batch *
+  // row blocks).
+  int pair_rows;
   // A decode step with the KV-cache append folded in (matrix-core kernel,
   // n_q = 1): each sequence's new row (fp32 [B][1][n_kv_head][HD]) is written
   // at position positions[b] into the caches k_app / v_app (the same buffers

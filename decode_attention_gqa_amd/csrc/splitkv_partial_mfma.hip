@@ -402,18 +402,31 @@ partial_mfma_kernel(PartialArgs a) {
   static_assert(CB == 1 || HD <= 128, "two column blocks: hd 64 and 128");
   static_assert(!PER_HEAD || (G == 1 && R == 1), "per-head form: one head");
   static_assert(!FOLD || (!PER_HEAD && R == 1), "folded append: one row");
-  const int sp = blockIdx.x;
-  const int hy = blockIdx.y;                         // first query head / G
-  const int hk = PER_HEAD ? hy / a.kv_group : hy;    // KV head
-  // (sequence, first query row of this workgroup)
+  // split, first query head / G, and (sequence, first query row of this
+  // workgroup)
+  int sp_ = blockIdx.x;
+  int hy_ = blockIdx.y;
   detail::RowSel rs;
   if constexpr (R == 1) {
     rs = detail::row_sel(a);
+  } else if (a.pair_rows) {
+    // grid dim3(8 * row blocks, n_splits / 8, n_kv_head * batch): the row
+    // blocks of one (split, KV head, sequence) are 8 apart in the dispatch
+    // order, which deals workgroups to the XCDs in turn, so they run on one
+    // XCD at the same time and the later reads of each K/V tile are served
+    // by its L2
+    sp_ = (int)(blockIdx.x & 7u) + 8 * (int)blockIdx.y;
+    rs.b = blockIdx.z / a.n_kv_head;
+    hy_ = blockIdx.z - rs.b * a.n_kv_head;
+    rs.t = (int)(blockIdx.x >> 3) * R;
   } else {
     const int nrb = (a.n_q + R - 1) / R;
     rs.b = blockIdx.z / nrb;
     rs.t = (blockIdx.z - rs.b * nrb) * R;
   }
+  const int sp = sp_;
+  const int hy = hy_;
+  const int hk = PER_HEAD ? hy / a.kv_group : hy;    // KV head
   const int b = rs.b;
   const int tid = threadIdx.x;
   // wave index, provably uniform (scalar) so per-tile row math stays scalar
@@ -774,10 +787,19 @@ hipError_t launch_hd(int group, const PartialArgs &a, int batch,
 }
 
 template <int HD, int G, int R>
-hipError_t launch_rows(const PartialArgs &a, int batch, hipStream_t stream) {
+hipError_t launch_rows(const PartialArgs &args, int batch,
+                       hipStream_t stream) {
+  PartialArgs a = args;
   const int nrb = (a.n_q + R - 1) / R;
-  hipLaunchKernelGGL((partial_mfma_kernel<HD, G, false, R>),
-                     dim3(a.n_splits, a.n_kv_head, batch * nrb),
+  // With several blocks of rows the blocks of one split read the same K/V
+  // rows; the paired grid runs them side by side on one XCD (at 32K rows,
+  // 28q/4kv, 4 rows: 21.8 against 24.9 us per layer with the plain grid).
+  a.pair_rows = nrb > 1 && a.n_splits % 8 == 0 &&
+                (long long)a.n_kv_head * batch <= 65535;
+  const dim3 grid = a.pair_rows
+                        ? dim3(8 * nrb, a.n_splits / 8, a.n_kv_head * batch)
+                        : dim3(a.n_splits, a.n_kv_head, batch * nrb);
+  hipLaunchKernelGGL((partial_mfma_kernel<HD, G, false, R>), grid,
                      dim3(kThreads), 0, stream, a);
   return hipGetLastError();
 }

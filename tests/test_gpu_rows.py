@@ -50,7 +50,9 @@ def test_rows_parity(hd):
             q, k, v, p = _rows_case(hd + 10 * G + n_q, 4, n_q, nh, nkvh, hd, T, pos)
             scale = float(np.float32(1 / np.sqrt(hd)))
             want = oracle.decode_attn_rows(q, k, v, p, nkvh, scale)
-            for S, blk in ((1, 0), (7, 0), (10, 32)):
+            # split counts that are multiples of 8 launch the blocks of rows
+            # of one split side by side (the paired grid)
+            for S, blk in ((1, 0), (7, 0), (10, 32), (16, 0), (8, 64)):
                 say(f"rows hd={hd} G={G} n_q={n_q} S={S} blk={blk}")
                 got, rec = _run_rows(q, k, v, p, S, blk, scale)
                 parity(got, want, f"rows hd={hd} G={G} n_q={n_q} S={S}")
