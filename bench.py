@@ -793,8 +793,9 @@ def run_rows(args):
     """Several query rows per sequence (speculative verification shape):
     28 layers of partial + combine in one graph, n_q rows per sequence at
     several live lengths, for the head layout given by --rows-heads (query
-    heads, KV heads; hd128). The split count comes from the heuristic for
-    several rows (splitkv_pick_splits_rows)."""
+    heads, KV heads) and head size --rows-hd. The split count comes from
+    the heuristic for several rows (splitkv_pick_splits_rows), plus those
+    given by --extra-splits."""
     import torch
 
     import decode_attention_gqa_amd as skv
@@ -802,7 +803,8 @@ def run_rows(args):
     cu = torch.cuda.get_device_properties(0).multi_processor_count
     max_ctx = synth.CFG3.max_ctx
     nh, nkvh = args.rows_heads
-    sh = synth.Shape(1, nh, nkvh, 128, max_ctx)
+    hd = args.rows_hd
+    sh = synth.Shape(1, nh, nkvh, hd, max_ctx)
     log(f"[bench] generating layer data: {nh}q/{nkvh}kv max_ctx={max_ctx}")
     base = Layers(args.layers, max_ctx, 1, 0, sh,
                   synth.make_case(3, sh, max_ctx))
@@ -810,42 +812,43 @@ def run_rows(args):
     g = torch.Generator(device=dev)
     g.manual_seed(4)
     for n_q in args.rows:
-        S, blk = skv.pick_splits_rows(1, n_q, nh, nkvh, 128, max_ctx, cu)
-        qs = [torch.randn((1, n_q, nh, 128), generator=g, device=dev)
-              for _ in range(base.L)]
-        parts = [torch.empty(skv.partials_bytes(1, n_q * nh, 128, S) // 4,
-                             device=dev) for _ in range(base.L)]
-        outs = [torch.empty((1, n_q, nh, 128), device=dev)
-                for _ in range(base.L)]
+        S_h, blk = skv.pick_splits_rows(1, n_q, nh, nkvh, hd, max_ctx, cu)
+        for S in [S_h] + [x for x in args.extra_splits if x != S_h]:
+            qs = [torch.randn((1, n_q, nh, hd), generator=g, device=dev)
+                  for _ in range(base.L)]
+            parts = [torch.empty(skv.partials_bytes(1, n_q * nh, hd, S) // 4,
+                                 device=dev) for _ in range(base.L)]
+            outs = [torch.empty((1, n_q, nh, hd), device=dev)
+                    for _ in range(base.L)]
 
-        def step():
-            for l in range(base.L):
-                skv.decode_attn_rows(qs[l], base.k[l], base.v[l], base.pos,
-                                     parts[l], outs[l], S, blk, base.scale)
+            def step():
+                for l in range(base.L):
+                    skv.decode_attn_rows(qs[l], base.k[l], base.v[l], base.pos,
+                                         parts[l], outs[l], S, blk, base.scale)
 
-        side = torch.cuda.Stream()
-        side.wait_stream(torch.cuda.current_stream())
-        with torch.cuda.stream(side):
-            step()
-        torch.cuda.current_stream().wait_stream(side)
-        torch.cuda.synchronize()
-        graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(graph):
-            step()
-        torch.cuda.synchronize()
-        for nkv in args.points:
-            base.set_nkv(nkv)
-            per, _, _ = time_replays(torch, graph, args.warmup, args.steps)
-            med = statistics.median(per)
-            kv = synth.kv_bytes(nkvh, 128, nkv) * base.L
-            print(json.dumps({"heads": f"{nh}q/{nkvh}kv", "rows": n_q,
-                              "n_splits": S, "nkv": nkv,
-                              "us_per_layer": round(med * 1e3 / base.L, 3),
-                              "us_per_row_layer": round(med * 1e3 / base.L / n_q, 3),
-                              "kv_gbps_once": round(kv / (med * 1e-3) / 1e9, 1)}),
-                  flush=True)
-        del graph, qs, parts, outs
-        torch.cuda.empty_cache()
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                step()
+            torch.cuda.current_stream().wait_stream(side)
+            torch.cuda.synchronize()
+            graph = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(graph):
+                step()
+            torch.cuda.synchronize()
+            for nkv in args.points:
+                base.set_nkv(nkv)
+                per, _, _ = time_replays(torch, graph, args.warmup, args.steps)
+                med = statistics.median(per)
+                kv = synth.kv_bytes(nkvh, hd, nkv) * base.L
+                print(json.dumps({"heads": f"{nh}q/{nkvh}kv", "hd": hd, "rows": n_q,
+                                  "n_splits": S, "heuristic": S == S_h, "nkv": nkv,
+                                  "us_per_layer": round(med * 1e3 / base.L, 3),
+                                  "us_per_row_layer": round(med * 1e3 / base.L / n_q, 3),
+                                  "kv_gbps_once": round(kv / (med * 1e-3) / 1e9, 1)}),
+                      flush=True)
+            del graph, qs, parts, outs
+            torch.cuda.empty_cache()
 
 
 def run_sweep(args):
@@ -962,7 +965,9 @@ def main():
     ap.add_argument("--rows", type=int, nargs="*", default=[1, 2, 4, 8],
                     help="--mode rows: query rows per sequence to time")
     ap.add_argument("--rows-heads", type=int, nargs=2, default=[28, 4],
-                    help="--mode rows: query heads and KV heads (hd128)")
+                    help="--mode rows: query heads and KV heads")
+    ap.add_argument("--rows-hd", type=int, default=128,
+                    help="--mode rows: head size")
     ap.add_argument("--per-head", action="store_true",
                     help="--mode kernels: time the per-query-head partial form")
     ap.add_argument("--extra-splits", type=int, nargs="*", default=[],

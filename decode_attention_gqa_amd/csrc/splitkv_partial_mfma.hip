@@ -407,9 +407,7 @@ partial_mfma_kernel(PartialArgs a) {
   int sp_ = blockIdx.x;
   int hy_ = blockIdx.y;
   detail::RowSel rs;
-  if constexpr (R == 1) {
-    rs = detail::row_sel(a);
-  } else if (a.pair_rows) {
+  if (a.pair_rows) {
     // grid dim3(8 * row blocks, n_splits / 8, n_kv_head * batch): the row
     // blocks of one (split, KV head, sequence) are 8 apart in the dispatch
     // order, which deals workgroups to the XCDs in turn, so they run on one
@@ -419,6 +417,8 @@ partial_mfma_kernel(PartialArgs a) {
     rs.b = blockIdx.z / a.n_kv_head;
     hy_ = blockIdx.z - rs.b * a.n_kv_head;
     rs.t = (int)(blockIdx.x >> 3) * R;
+  } else if constexpr (R == 1) {
+    rs = detail::row_sel(a);
   } else {
     const int nrb = (a.n_q + R - 1) / R;
     rs.b = blockIdx.z / nrb;
@@ -757,16 +757,33 @@ partial_mfma_kernel(PartialArgs a) {
   }
 }
 
+// Grid of the grouped kernel with `blocks` workgroups (blocks of query rows)
+// per (split, KV head, sequence). With more than one, the blocks of one split
+// read the same K/V rows, and the paired grid runs them side by side on one
+// XCD (at 32K rows, 28q/4kv hd128, 4 rows: 21.5 against 24.9 us per layer
+// with the plain grid); it needs a split count that is a multiple of 8.
+PartialArgs with_row_grid(const PartialArgs &args, int blocks, int batch,
+                          dim3 &grid) {
+  PartialArgs a = args;
+  a.pair_rows = blocks > 1 && a.n_splits % 8 == 0 &&
+                (long long)a.n_kv_head * batch <= 65535;
+  grid = a.pair_rows ? dim3(8 * blocks, a.n_splits / 8, a.n_kv_head * batch)
+                     : dim3(a.n_splits, a.n_kv_head, batch * blocks);
+  return a;
+}
+
 template <int HD, int G>
 hipError_t launch_one(const PartialArgs &a, int batch, hipStream_t stream) {
-  if (a.k_new != nullptr)
+  if (a.k_new != nullptr) {
     hipLaunchKernelGGL((partial_mfma_kernel<HD, G, false, 1, true>),
                        dim3(a.n_splits, a.n_kv_head, batch), dim3(kThreads),
                        0, stream, a);
-  else
-    hipLaunchKernelGGL((partial_mfma_kernel<HD, G>),
-                       dim3(a.n_splits, a.n_kv_head, batch * a.n_q),
-                       dim3(kThreads), 0, stream, a);
+  } else {
+    dim3 grid;
+    const PartialArgs b = with_row_grid(a, a.n_q, batch, grid);
+    hipLaunchKernelGGL((partial_mfma_kernel<HD, G>), grid, dim3(kThreads), 0,
+                       stream, b);
+  }
   return hipGetLastError();
 }
 
@@ -787,20 +804,11 @@ hipError_t launch_hd(int group, const PartialArgs &a, int batch,
 }
 
 template <int HD, int G, int R>
-hipError_t launch_rows(const PartialArgs &args, int batch,
-                       hipStream_t stream) {
-  PartialArgs a = args;
-  const int nrb = (a.n_q + R - 1) / R;
-  // With several blocks of rows the blocks of one split read the same K/V
-  // rows; the paired grid runs them side by side on one XCD (at 32K rows,
-  // 28q/4kv, 4 rows: 21.8 against 24.9 us per layer with the plain grid).
-  a.pair_rows = nrb > 1 && a.n_splits % 8 == 0 &&
-                (long long)a.n_kv_head * batch <= 65535;
-  const dim3 grid = a.pair_rows
-                        ? dim3(8 * nrb, a.n_splits / 8, a.n_kv_head * batch)
-                        : dim3(a.n_splits, a.n_kv_head, batch * nrb);
+hipError_t launch_rows(const PartialArgs &a, int batch, hipStream_t stream) {
+  dim3 grid;
+  const PartialArgs b = with_row_grid(a, (a.n_q + R - 1) / R, batch, grid);
   hipLaunchKernelGGL((partial_mfma_kernel<HD, G, false, R>), grid,
-                     dim3(kThreads), 0, stream, a);
+                     dim3(kThreads), 0, stream, b);
   return hipGetLastError();
 }
 
