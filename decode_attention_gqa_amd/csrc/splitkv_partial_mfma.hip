@@ -274,6 +274,10 @@ __device__ __forceinline__ void compute_tile(
     float &s_run, int col, int grp, int lane, bool hi_col) {
   using Geo = MGeo<HD>;
   unsigned char *vlds = slice + Geo::KTILE;
+  // Raised issue priority while a landed tile is computed: the wave's next
+  // loads wait for this compute (28 layers at 32K rows: 16.37 against 16.45
+  // us per layer without it).
+  __builtin_amdgcn_s_setprio(2);
   // a4: scores S = K · Q'ᵀ, K operands read back from the staged rows.
   stage_rows<HD, Geo::KSTR>(t.k, slice, lane);
   uint4 ka[Geo::KS];
@@ -365,6 +369,7 @@ __device__ __forceinline__ void compute_tile(
       oacc[cb][b] = __builtin_amdgcn_mfma_f32_16x16x16f16(
           __builtin_bit_cast(half4, r0), pf[cb], oacc[cb][b], 0, 0, 0);
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // A column's output: hi part + lo part. One block: this lane's column plus
