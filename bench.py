@@ -57,6 +57,7 @@ if ROOT not in sys.path:
 
 METRIC = "KV-stream GB/s (% of HBM peak) + µs/layer, 28q/4kv hd128 decode @2K–32K"
 HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 * 1000 * 1000   # MI355X Infinity Cache (256 MB)
 CSRC = os.path.join(ROOT, "decode_attention_gqa_amd", "csrc")
 PARTIAL_SRCS = [os.path.join(CSRC, f) for f in (
     "splitkv_partial.hip", "splitkv_partial_mfma.hip",
@@ -252,8 +253,21 @@ def hbm_read_probe(torch, skv, gib: float = 4.0, reps: int = 5) -> float:
     return best
 
 
-def cpu_baseline(lay: Layers, nkv: int, budget_s: float = 12.0) -> dict:
-    """The fp64 oracle (one thread) on one layer at the same live length."""
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(lay: Layers, nkv: int, budget_s: float = 12.0):
+    """The fp64 oracle (one thread) on one layer at the same live length.
+    Returns (the cpu_baseline record, the oracle's output of that layer)."""
     import numpy as np
 
     import oracle
@@ -263,16 +277,34 @@ def cpu_baseline(lay: Layers, nkv: int, budget_s: float = 12.0) -> dict:
     kv = synth.kv_bytes(lay.shape.n_kv_head, lay.shape.head_dim, nkv)
     runs, t0 = 0, time.perf_counter()
     while True:
-        oracle.decode_attn(c.q, c.k, c.v, pos, lay.shape.n_kv_head, c.scale)
+        ref = oracle.decode_attn(c.q, c.k, c.v, pos, lay.shape.n_kv_head,
+                                 c.scale)
         runs += 1
         el = time.perf_counter() - t0
         if el >= budget_s or runs >= 50:
             break
+    model = cpu_model()
     return {"value": round(kv * runs / el / 1e9, 4), "unit": "GB/s",
-            "cores": 1, "kind": "oracle",
+            "cores": 1, "kind": "oracle", "cpu_model": model,
+            "cpus_visible": os.cpu_count(),
             "sample": f"{runs} x one layer (28q/4kv hd128, nkv {nkv}) in "
-                      f"{el:.1f} s, single-threaded fp64 C, host "
-                      f"{os.cpu_count()} cpus visible"}
+                      f"{el:.1f} s, single-threaded fp64 C on one core of "
+                      f"{model} ({os.cpu_count()} cpus visible)"}, ref
+
+
+def worst_errors(got, ref) -> dict:
+    """Largest abs and rel error of a GPU output against the oracle's (rel
+    over elements with |oracle| > 1e-6), and whether every element meets the
+    bar |err| <= 5e-5 or |err| <= 1e-3 |oracle|."""
+    import numpy as np
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    err = np.abs(got - ref)
+    big = np.abs(ref) > 1e-6
+    rel = np.where(big, err / np.where(big, np.abs(ref), 1.0), 0.0)
+    ok = bool(np.all((err <= 5e-5) | (err <= 1e-3 * np.abs(ref))))
+    return {"max_abs": float(err.max()), "max_rel": float(rel.max()),
+            "within_bar": ok}
 
 
 def load_traffic(nkv: int, n_splits: int, block_len: int):
@@ -310,16 +342,33 @@ def run_main(args):
     graph = lay.capture()
 
     points = []
+    flush = None
     for nkv in sorted(set(args.points + [args.nkv])):
         lay.set_nkv(nkv)
         per, total, _ = time_replays(torch, graph, args.warmup, args.steps)
         med = statistics.median(per)
         kv = synth.kv_bytes(4, 128, nkv) * args.layers
-        points.append({"nkv": nkv, "ms_per_step_median": round(med, 5),
-                       "us_per_layer": round(med * 1e3 / args.layers, 3),
-                       "kv_gbps": round(kv / (med * 1e-3) / 1e9, 1),
-                       "pct_hbm_peak": round(100 * kv / (med * 1e-3) / 1e9 /
-                                             HBM_PEAK_GBPS, 2)})
+        pt = {"nkv": nkv, "ms_per_step_median": round(med, 5),
+              "us_per_layer": round(med * 1e3 / args.layers, 3),
+              "kv_gbps": round(kv / (med * 1e-3) / 1e9, 1),
+              "pct_hbm_peak": round(100 * kv / (med * 1e-3) / 1e9 /
+                                    HBM_PEAK_GBPS, 2),
+              "working_set_mb": round(kv / 1e6, 1)}
+        if kv <= MALL_BYTES:
+            # The whole step's K/V fits the Infinity Cache: the replays
+            # above read it from there (warm). Cold: a 1 GiB read of other
+            # data runs before each replay, outside the timed window.
+            if flush is None:
+                flush = make_flush(torch, skv)
+            cold = statistics.median(time_replays_cold(
+                torch, graph, flush, args.warmup, args.steps))
+            pt.update({"resident": "Infinity Cache (warm)",
+                       "us_per_layer_cold": round(cold * 1e3 / args.layers, 3),
+                       "pct_hbm_peak_cold": round(
+                           100 * kv / (cold * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2)})
+        else:
+            pt["resident"] = "HBM"
+        points.append(pt)
         log(f"[bench] nkv={nkv}: {points[-1]}")
 
     # headline: the timed K steps at --nkv
@@ -336,7 +385,13 @@ def run_main(args):
     traffic, traffic_src = load_traffic(args.nkv, S, blk)
     probe = hbm_read_probe(torch, skv) if not args.no_probe else None
 
-    cpu = cpu_baseline(lay, args.nkv, args.cpu_budget) if not args.no_cpu else None
+    cpu, parity = None, None
+    if not args.no_cpu:
+        cpu, ref = cpu_baseline(lay, args.nkv, args.cpu_budget)
+        # layer 0's output from the timed replays against the oracle's
+        parity = worst_errors(lay.out[0].cpu().numpy(), ref)
+        parity["sample"] = (f"layer 0 of the timed graph at nkv {args.nkv}, "
+                            f"all 28 x 128 outputs")
     # every byte a layer moves: q, K+V, the records written by the partial
     # kernel and read back by the combine, and the output
     rec_bytes = skv.partials_bytes(1, 28, 128, S)
@@ -352,14 +407,19 @@ def run_main(args):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "fp16",
         "data": "synthetic",
         "config": {"workload": f"decode attention 28q/4kv hd128, nkv {args.nkv}, "
                                f"{args.layers} layers with separate KV buffers, "
                                f"hipGraph of partial+combine",
                    "nkv": args.nkv, "layers": args.layers, "max_ctx": max_ctx,
                    "n_splits": S, "block_len": blk, "kv_dtype": "fp16",
-                   "q_acc_dtype": "fp32", "global_batch": 1},
+                   "q_dtype": "fp32", "out_dtype": "fp32",
+                   "contraction": "fp16 matrix cores (v_mfma_f32_16x16x32_f16 "
+                                  "for q.K, v_mfma_f32_16x16x16_f16 for p.V), "
+                                  "fp32 accumulation; q and p as fp16 hi+lo "
+                                  "pairs (about 22 significant bits)",
+                   "global_batch": 1},
         "us_per_layer": round(ms_step * 1e3 / args.layers, 3),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1),
@@ -378,6 +438,7 @@ def run_main(args):
         "total_gbps": round(total_layer * args.layers / (ms_step * 1e-3) / 1e9, 1),
         "points": points,
         "cpu_baseline": cpu,
+        "parity_vs_oracle": parity,
         "wall_s_timed": round(wall, 4),
         "device": props.name,
         "cu_count": cu,

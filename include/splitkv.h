@@ -55,6 +55,19 @@
  * [sp*chunk, min(nkv_b, sp*chunk + chunk)); a split with no rows writes
  * (-inf, 0, lo, hi, 0...) and contributes exactly zero to the merge.
  *
+ * Precision and the query range. K and V are used exactly as stored (fp16).
+ * For head_dim 8/16/32 the scores and the output are computed in fp32 vector
+ * arithmetic from the fp32 q. For head_dim 64/128/256 both products run on
+ * the fp16 matrix cores with fp32 accumulation: each element of
+ * q' = q * scale * log2(e) enters as an fp16 pair hi = fp16(q'), lo =
+ * fp16(q' - hi), so it is carried to about max(2^-22 |q'|, 2^-24), and the
+ * softmax weights p likewise as hi + lo pairs. This requires every |q'| to
+ * stay below 65504 (the fp16 range of the hi part: larger values become
+ * infinite and the output is undefined) and q to be finite; q is device
+ * memory, so the host does not check it. Within that range the output meets
+ * |err| <= 5e-5 or |err| <= 1e-3 |exact| per element against an exact
+ * evaluation of the definition (tested with q up to 4000 x N(0, 1)).
+ *
  * Supported shapes: head_dim in {8, 16, 32, 64, 128, 256}; G = n_head /
  * n_kv_head in 1..8; n_splits in 1..65535; n_kv_head and batch <= 65535;
  * max_ctx + n_splits < 2^31; (max_ctx + 64) * n_kv_head * head_dim * 2 bytes
@@ -163,7 +176,13 @@ int splitkv_partial(const float *q, const uint16_t *k_cache,
  * splitkv_partial / splitkv_decode_attn, plus SPLITKV_EINVAL when n_q < 1,
  * batch * n_q > 65535 or n_q * n_head > 65535. n_q = 1 is exactly
  * splitkv_partial / splitkv_decode_attn. The combine of these records is
- * splitkv_combine with n_head -> n_q * n_head. */
+ * splitkv_combine with n_head -> n_q * n_head.
+ * Restriction: rows that share a workgroup multiply every staged V row into
+ * every row's output with a weight of exactly 0 where the row is not yet
+ * visible, so a non-finite V value in one of the n_q - 1 newest cache rows
+ * (e.g. an fp16 overflow in the appended values) turns the outputs of the
+ * earlier query rows of that block into NaN, where the definition leaves
+ * them finite. Finite caches are unaffected. */
 int splitkv_partial_rows(const float *q, const uint16_t *k_cache,
                          const uint16_t *v_cache, const int32_t *positions,
                          float *partials, int batch, int n_q, int n_head,

@@ -13,6 +13,11 @@ import numpy as np
 ABS_TOL = 5e-5
 REL_TOL = 1e-3
 
+# Worst errors seen per workload over the session: {label: [max abs, max rel,
+# elements compared]}. conftest.py prints the table at the end of the run and,
+# when SPLITKV_PARITY_LOG names a file, writes it there as JSON.
+WORST: dict = {}
+
 
 def say(*parts):
     """Name the case about to run on the GPU, flushed, so a crash log shows it."""
@@ -64,8 +69,11 @@ def run_gpu(case, n_splits, block_len=0, dev=None):
     return out.cpu().numpy(), rec
 
 
-def parity(got, ref, what=""):
-    """Assert the parity bar; returns (max abs err, max rel err)."""
+def parity(got, ref, what="", cfg=None):
+    """Assert the parity bar; returns (max abs err, max rel err). With `cfg`
+    (a workload label) the errors also count towards that workload's worst
+    case in WORST. The relative error is taken over elements with
+    |oracle| > 1e-6."""
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     assert got.shape == ref.shape, (got.shape, ref.shape)
@@ -78,11 +86,18 @@ def parity(got, ref, what=""):
         raise AssertionError(
             f"{what}: {int((~ok).sum())} of {ok.size} outside the bar; worst at "
             f"{idx}: gpu {got[idx]!r} oracle {ref[idx]!r} abs {err[idx]:.3e}")
-    return float(err.max()) if err.size else 0.0, \
-        float(np.where(np.abs(ref) > 1e-6, rel, 0).max()) if rel.size else 0.0
+    worst_abs = float(err.max()) if err.size else 0.0
+    worst_rel = float(np.where(np.abs(ref) > 1e-6, rel, 0).max()) \
+        if rel.size else 0.0
+    if cfg is not None:
+        w = WORST.setdefault(cfg, [0.0, 0.0, 0])
+        w[0] = max(w[0], worst_abs)
+        w[1] = max(w[1], worst_rel)
+        w[2] += int(err.size)
+    return worst_abs, worst_rel
 
 
-def check_records(rec_gpu, rec_ref, what=""):
+def check_records(rec_gpu, rec_ref, what="", cfg=None):
     """Records: lo/hi bit-exact, idle slots exact, mx / S / oc/S within the bar."""
     lohi = rec_gpu[..., 2:4].copy().view(np.int32)
     assert np.array_equal(lohi, rec_ref[..., 2:4].astype(np.int32)), \
@@ -94,8 +109,9 @@ def check_records(rec_gpu, rec_ref, what=""):
     assert np.all(rec_gpu[..., 4:][idle] == 0.0)
     live = ~idle
     if live.any():
-        parity(rec_gpu[..., 0][live], rec_ref[..., 0][live], what + " mx")
-        parity(rec_gpu[..., 1][live], rec_ref[..., 1][live], what + " S")
+        rc = None if cfg is None else cfg + " records"
+        parity(rec_gpu[..., 0][live], rec_ref[..., 0][live], what + " mx", rc)
+        parity(rec_gpu[..., 1][live], rec_ref[..., 1][live], what + " S", rc)
         parity(rec_gpu[..., 4:][live] / rec_gpu[..., 1][live][:, None],
                rec_ref[..., 4:][live] / rec_ref[..., 1][live][:, None],
-               what + " oc/S")
+               what + " oc/S", rc)

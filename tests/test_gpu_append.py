@@ -125,6 +125,7 @@ def test_decode_step_graph():
             torch.cuda.synchronize()
         ck, cv = oracle.append_kv(kn, vn, ck, cv, pos)
         want = oracle.decode_attn(q, ck, cv, pos, nkvh, scale)
-        parity(out.cpu().numpy(), want, f"decode step {i}")
+        parity(out.cpu().numpy(), want, f"decode step {i}",
+               "append + attention graph")
     _f16_equal(dk.cpu().numpy(), ck, "K after 12 steps")
     _f16_equal(dv.cpu().numpy(), cv, "V after 12 steps")

@@ -43,7 +43,7 @@ def test_combine_alone(hd):
         torch.cuda.synchronize()
         got = out.cpu().numpy()
         assert np.array_equal(got[0, 0], np.zeros(hd, np.float32))
-        parity(got, want, f"combine hd={hd} S={S}")
+        parity(got, want, f"combine hd={hd} S={S}", "combine alone")
 
 
 def test_graph_replay_growing_context():
@@ -96,7 +96,8 @@ def test_graph_replay_growing_context():
             c.positions[:] = nkv - 1
             ref = oracle.decode_attn(c.q, c.k, c.v, c.positions, sh.n_kv_head,
                                      c.scale)
-            parity(got[l], ref, f"replay nkv={nkv} layer={l}")
+            parity(got[l], ref, f"replay nkv={nkv} layer={l}",
+                   "3 growing, graph replays")
             if nkv == 1:
                 for h in range(sh.n_head):
                     assert np.array_equal(

@@ -74,7 +74,8 @@ def test_folded_step_equals_separate_calls(hd, nh, nkvh):
         _bits_equal(k_f, ck, f"K vs oracle hd={hd} S={S}")
         _bits_equal(v_f, cv, f"V vs oracle hd={hd} S={S}")
         _bits_equal(o_fold, o_sep, f"out hd={hd} S={S}")
-        parity(o_fold, want, f"decode step hd={hd} S={S} blk={blk}")
+        parity(o_fold, want, f"decode step hd={hd} S={S} blk={blk}",
+               "decode step (append folded)")
 
 
 def test_folded_step_graph():
@@ -130,6 +131,7 @@ def test_folded_step_graph():
             torch.cuda.synchronize()
         ck, cv = oracle.append_kv(kn, vn, ck, cv, pos)
         want = oracle.decode_attn(q, ck, cv, pos, nkvh, scale)
-        parity(out.cpu().numpy(), want, f"folded step {i}")
+        parity(out.cpu().numpy(), want, f"folded step {i}",
+               "decode step (append folded)")
     _bits_equal(dk.cpu().numpy(), ck, "K after 12 steps")
     _bits_equal(dv.cpu().numpy(), cv, "V after 12 steps")

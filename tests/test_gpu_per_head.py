@@ -52,4 +52,5 @@ def test_per_head_equals_grouped(hd):
                     f"differ; heads {heads}; fields {fields} (4 = oc); max "
                     f"abs diff {mad:.3e}; first {idx[0].tolist()} grouped "
                     f"{ra[tuple(idx[0])]!r} per-head {rb[tuple(idx[0])]!r}")
-            parity(out.cpu().numpy(), want, f"per-head hd={hd} G={G} S={S}")
+            parity(out.cpu().numpy(), want, f"per-head hd={hd} G={G} S={S}",
+                   "per-query-head grid")

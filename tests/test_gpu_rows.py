@@ -55,7 +55,8 @@ def test_rows_parity(hd):
             for S, blk in ((1, 0), (7, 0), (10, 32), (16, 0), (8, 64)):
                 say(f"rows hd={hd} G={G} n_q={n_q} S={S} blk={blk}")
                 got, rec = _run_rows(q, k, v, p, S, blk, scale)
-                parity(got, want, f"rows hd={hd} G={G} n_q={n_q} S={S}")
+                parity(got, want, f"rows hd={hd} G={G} n_q={n_q} S={S}",
+                       "rows n_q 1..8, 300 rows")
                 # slots [2],[3]: the split bounds of the last row's length
                 for b in range(4):
                     lo, hi = oracle.split_bounds(
@@ -68,6 +69,38 @@ def test_rows_parity(hd):
                 # a row before position 0 sees no keys: exactly 0
                 if n_q > 2:
                     assert np.all(got[3, 0] == 0.0)
+
+
+@pytest.mark.parametrize("n_q", [4, 8])
+def test_rows_full_length(n_q):
+    """The verification shape at the full cache length: 28q/4kv hd 128,
+    max_ctx 33,024, two sequences whose last rows sit at 32,767 and 30,000,
+    n_q query rows each, at the heuristic's split count (a multiple of 8, so
+    the blocks of rows of one split run side by side) and at 64 splits; rows
+    past each sequence's end are fp16 NaN so that a read past a row's end
+    shows up."""
+    import decode_attention_gqa_amd as skv
+    B, nh, nkvh, hd, T = 2, 28, 4, 128, 33024
+    pos = [32767, 30000]
+    q, k, v, p = _rows_case(50 + n_q, B, n_q, nh, nkvh, hd, T, pos)
+    for b in range(B):
+        k[b, pos[b] + 1:].view(np.uint16)[...] = 0x7E00
+        v[b, pos[b] + 1:].view(np.uint16)[...] = 0x7E00
+    scale = float(np.float32(1 / np.sqrt(hd)))
+    say(f"rows full length n_q={n_q}: oracle")
+    want = oracle.decode_attn_rows(q, k, v, p, nkvh, scale)
+    S_h, blk_h = skv.pick_splits_rows(B, n_q, nh, nkvh, hd, T, 256)
+    assert S_h % 8 == 0, S_h
+    for S, blk in ((S_h, blk_h), (64, 0)):
+        say(f"rows full length n_q={n_q} S={S}")
+        got, rec = _run_rows(q, k, v, p, S, blk, scale)
+        parity(got, want, f"rows full length n_q={n_q} S={S}",
+               "rows n_q 4/8, 28q/4kv at 32K")
+        for b in range(B):
+            lo, hi = oracle.split_bounds(pos[b] + 1, S, blk)
+            lohi = rec[b, :, 0, 2:4].copy().view(np.int32)
+            assert np.array_equal(lohi[:, 0], lo) and \
+                np.array_equal(lohi[:, 1], hi)
 
 
 def test_one_row_equals_decode():
@@ -146,4 +179,5 @@ def test_speculative_verify_graph():
             torch.cuda.synchronize()
         ck, cv = oracle.append_kv(kn, vn, ck, cv, pos)
         want = oracle.decode_attn_rows(q, ck, cv, pos, nkvh, scale)
-        parity(out.cpu().numpy(), want, f"verify step {i}")
+        parity(out.cpu().numpy(), want, f"verify step {i}",
+               "rows, verification graph")
