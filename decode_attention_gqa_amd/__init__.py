@@ -8,7 +8,8 @@ status into ``SplitKVError``. Every step of the computation runs in the HIP
 kernels. There is no fallback: if the library is missing, every call raises.
 
 Names follow the C ABI (``splitkv_`` dropped): ``decode_attn``,
-``decode_step``, ``decode_attn_rows``, ``partial``, ``partial_rows``,
+``decode_attn_noalloc``, ``decode_step``, ``decode_attn_rows``,
+``partial``, ``partial_rows``,
 ``partial_per_head``, ``combine``, ``append_kv``, ``partials_bytes``,
 ``pick_splits``, ``pick_splits_rows``, ``workgroups_per_cu``, ``strerror``,
 ``probe_read``, ``probe_copy``.
@@ -22,7 +23,8 @@ import threading
 
 __all__ = ["SplitKVError", "load", "abi_version", "strerror", "partials_bytes",
            "pick_splits", "pick_splits_rows", "partial", "partial_per_head",
-           "partial_rows", "combine", "decode_attn", "decode_attn_rows",
+           "partial_rows", "combine", "decode_attn", "decode_attn_noalloc",
+           "decode_attn_rows", "NOALLOC_SCRATCH_BYTES",
            "decode_step", "append_kv", "workgroups_per_cu", "probe_read",
            "probe_copy", "LIB_PATH", "SUPPORTED_HEAD_DIMS", "MAX_GROUP"]
 
@@ -30,7 +32,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
                         "libsplitkv.so")
 SUPPORTED_HEAD_DIMS = (8, 16, 32, 64, 128, 256)
 MAX_GROUP = 8
-ABI_VERSION = 1
+ABI_VERSION = 2
+NOALLOC_SCRATCH_BYTES = 16 << 20   # SPLITKV_NOALLOC_SCRATCH_BYTES
 
 _lock = threading.Lock()
 _lib = None
@@ -61,6 +64,8 @@ SIGNATURES = {
     "splitkv_combine": (_i, [_vp, _vp, _i, _i, _i, _i, _vp]),
     "splitkv_decode_attn": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i,
                                  _i, _i, _i, _f, _vp]),
+    "splitkv_decode_attn_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i,
+                                         _i, _i, _i, _i, _f, _vp]),
     "splitkv_append_kv": (_i, [_vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i,
                                _vp]),
     "splitkv_decode_step": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i,
@@ -312,6 +317,25 @@ def decode_attn(q, k_cache, v_cache, positions, partials, out, n_splits: int,
         positions.data_ptr(), partials.data_ptr(), out.data_ptr(), B, nh, nkvh,
         hd, max_ctx, n_splits, block_len, scale, _stream_ptr(stream)),
         "splitkv_decode_attn")
+
+
+def decode_attn_noalloc(q, k_cache, v_cache, positions, out, n_splits: int,
+                        block_len: int = 0, scale: float | None = None,
+                        stream=None):
+    """decode_attn without a caller records buffer: the library keeps the
+    split records in its own device scratch (NOALLOC_SCRATCH_BYTES per GPU,
+    shared by every call on that GPU: calls that overlap on one GPU race)."""
+    torch = _torch()
+    B, nh, nkvh, hd, max_ctx = _shapes(q, k_cache, v_cache, positions)
+    _need(out, (torch.float32,), "out")
+    if tuple(out.shape) != (B, nh, hd):
+        raise ValueError("out must be [B][n_head][hd]")
+    scale = 1.0 / math.sqrt(hd) if scale is None else float(scale)
+    _check(load().splitkv_decode_attn_noalloc(
+        q.data_ptr(), k_cache.data_ptr(), v_cache.data_ptr(),
+        positions.data_ptr(), out.data_ptr(), B, nh, nkvh, hd, max_ctx,
+        n_splits, block_len, scale, _stream_ptr(stream)),
+        "splitkv_decode_attn_noalloc")
 
 
 def append_kv(k_new, v_new, k_cache, v_cache, positions, stream=None):

@@ -6,12 +6,23 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
 #include <climits>
 #include <cmath>
+#include <mutex>
 
 #include "splitkv.h"
 #include "splitkv_internal.h"
 #include "splitkv_probe.h"
+
+// Scratch of splitkv_decode_attn_noalloc: the split records of one call live
+// here instead of in a caller buffer. Every device that runs the library holds
+// its own copy (allocated when the code object is loaded, kept until the
+// process ends). In host code `scratch` names a host-side stand-in, not
+// device memory: kernels get the address that hipGetSymbolAddress returns for
+// the current device, resolved once per device and cached below.
+static __device__ __align__(256) float
+    scratch[SPLITKV_NOALLOC_SCRATCH_BYTES / sizeof(float)];
 
 namespace {
 
@@ -113,6 +124,34 @@ int do_partial(const float *q, const uint16_t *k, const uint16_t *v,
   return e == hipSuccess ? SPLITKV_OK : SPLITKV_ELAUNCH;
 }
 
+constexpr size_t kScratchBytes = SPLITKV_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::atomic<float *> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch` (first call on a device: one
+// hipGetSymbolAddress with that device current).
+int scratch_on_current_device(float **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return SPLITKV_ELAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return SPLITKV_EUNSUPPORTED;
+  float *p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      void *addr = nullptr;
+      if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess ||
+          addr == nullptr)
+        return SPLITKV_ELAUNCH;
+      p = static_cast<float *>(addr);
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return SPLITKV_OK;
+}
+
 int do_combine(const float *partials, float *out, int batch, int n_head,
                int head_dim, int n_splits, void *stream) {
   splitkv::CombineArgs a;
@@ -138,6 +177,8 @@ const char *splitkv_strerror(int status) {
     case SPLITKV_EUNSUPPORTED: return "unsupported head_dim or group size";
     case SPLITKV_EALIGN: return "misaligned pointer";
     case SPLITKV_ELAUNCH: return "kernel launch failed";
+    case SPLITKV_ESCRATCH:
+      return "split records exceed the allocation-free entry point's scratch";
     default: return "unknown status";
   }
 }
@@ -258,6 +299,36 @@ int splitkv_decode_attn(const float *q, const uint16_t *k_cache,
                   stream);
   if (st != SPLITKV_OK) return st;
   return do_combine(partials, out, batch, n_head, head_dim, n_splits, stream);
+}
+
+int splitkv_decode_attn_noalloc(const float *q, const uint16_t *k_cache,
+                                const uint16_t *v_cache,
+                                const int32_t *positions, float *out, int batch,
+                                int n_head, int n_kv_head, int head_dim,
+                                int max_ctx, int n_splits, int block_len,
+                                float scale, void *stream) {
+  if (!q || !k_cache || !v_cache || !positions || !out) return SPLITKV_EINVAL;
+  int st = check_shape(batch, n_head, n_kv_head, head_dim, max_ctx, n_splits,
+                       block_len);
+  if (st != SPLITKV_OK) return st;
+  st = check_combine_shape(batch, n_head, head_dim, n_splits);
+  if (st != SPLITKV_OK) return st;
+  if (!std::isfinite(scale)) return SPLITKV_EINVAL;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) ||
+      !aligned(out, 16) || !aligned(positions, 4))
+    return SPLITKV_EALIGN;
+  if (splitkv_partials_bytes(batch, n_head, head_dim, n_splits) > kScratchBytes)
+    return SPLITKV_ESCRATCH;
+  float *recs = nullptr;
+  st = scratch_on_current_device(&recs);
+  if (st != SPLITKV_OK) return st;
+  // The partial kernel writes every record of the call (idle splits too), so
+  // nothing left in the scratch by an earlier call is read.
+  st = do_partial(q, k_cache, v_cache, positions, recs, batch, n_head,
+                  n_kv_head, head_dim, max_ctx, n_splits, block_len, scale,
+                  stream);
+  if (st != SPLITKV_OK) return st;
+  return do_combine(recs, out, batch, n_head, head_dim, n_splits, stream);
 }
 
 int splitkv_partial_rows(const float *q, const uint16_t *k_cache,

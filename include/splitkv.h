@@ -89,8 +89,12 @@ extern "C" {
 #define SPLITKV_EUNSUPPORTED (-2) /* head_dim or group size not compiled      */
 #define SPLITKV_EALIGN (-3)       /* a pointer breaks its alignment rule      */
 #define SPLITKV_ELAUNCH (-4)      /* the HIP runtime refused a launch         */
+#define SPLITKV_ESCRATCH (-5)     /* records exceed the no-alloc scratch      */
 
-#define SPLITKV_ABI_VERSION 1
+#define SPLITKV_ABI_VERSION 2
+
+/* Capacity of the device-resident scratch of splitkv_decode_attn_noalloc. */
+#define SPLITKV_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 /* ABI version of the loaded library (SPLITKV_ABI_VERSION at build time). */
 int splitkv_abi_version(void);
@@ -223,6 +227,35 @@ int splitkv_decode_attn(const float *q, const uint16_t *k_cache,
                         float *partials, float *out, int batch, int n_head,
                         int n_kv_head, int head_dim, int max_ctx, int n_splits,
                         int block_len, float scale, void *stream);
+
+/* splitkv_decode_attn for callers that cannot allocate device memory (code
+ * under hipGraph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same partial and combine kernels, with the split records
+ * kept in a scratch array that the library holds in device memory instead of
+ * a caller `partials` buffer. The caller passes q, the caches, positions and
+ * out as for splitkv_decode_attn; nothing is allocated and no allocating
+ * routine is called.
+ *   Limit: the records, splitkv_partials_bytes(batch, n_head, head_dim,
+ *   n_splits), must fit SPLITKV_NOALLOC_SCRATCH_BYTES (16 MiB: e.g. up to
+ *   1,134 splits for one 28q hd128 sequence, 31 splits for 32 sequences of
+ *   32q hd128); larger requests return SPLITKV_ESCRATCH and enqueue nothing.
+ *   Sharing: each GPU holds one copy of the scratch (allocated when the
+ *   library's device code is loaded on it, kept until the process ends), and
+ *   every call on that GPU uses it, so calls that overlap on one GPU (several
+ *   streams, or several host threads) race and must be serialised by the
+ *   caller. Calls enqueued on one stream are ordered and safe. The scratch
+ *   keeps the last call's records; nothing in it needs clearing, because the
+ *   partial kernel writes every record of a call before the combine reads it.
+ *   The first call on each device resolves the scratch's device address once
+ *   (hipGetSymbolAddress with that device current); make that first call
+ *   outside graph capture.
+ * Other arguments, layouts and errors as for splitkv_decode_attn. */
+int splitkv_decode_attn_noalloc(const float *q, const uint16_t *k_cache,
+                                const uint16_t *v_cache,
+                                const int32_t *positions, float *out, int batch,
+                                int n_head, int n_kv_head, int head_dim,
+                                int max_ctx, int n_splits, int block_len,
+                                float scale, void *stream);
 
 /* KV-cache append, the step before attention in a decode step (dotLLM issue
  * #199, comment 1, section 1: the new K/V rows are written into the FP16

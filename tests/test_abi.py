@@ -12,7 +12,7 @@ import pytest
 import decode_attention_gqa_amd as skv
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-OK, EINVAL, EUNSUP, EALIGN, ELAUNCH = 0, -1, -2, -3, -4
+OK, EINVAL, EUNSUP, EALIGN, ELAUNCH, ESCRATCH = 0, -1, -2, -3, -4, -5
 
 
 def _declared_symbols():
@@ -38,9 +38,10 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strerror(lib):
-    assert lib.splitkv_abi_version() == 1
-    texts = {c: skv.strerror(c) for c in (OK, EINVAL, EUNSUP, EALIGN, ELAUNCH)}
-    assert len(set(texts.values())) == 5
+    assert lib.splitkv_abi_version() == 2
+    texts = {c: skv.strerror(c)
+             for c in (OK, EINVAL, EUNSUP, EALIGN, ELAUNCH, ESCRATCH)}
+    assert len(set(texts.values())) == 6
     assert skv.strerror(-99) == "unknown status"
 
 
@@ -219,6 +220,43 @@ def test_decode_rejects_bad_out(lib):
     a = _partial_args()
     assert _call_decode(lib, a, out=0) == EINVAL
     assert _call_decode(lib, a, out=A + 0x5000 + 4) == EALIGN
+
+
+def _call_noalloc(lib, a, out=A + 0x5000):
+    return lib.splitkv_decode_attn_noalloc(
+        a["q"], a["k"], a["v"], a["pos"], out, a["B"], a["nh"], a["nkvh"],
+        a["hd"], a["T"], a["S"], a["blk"], a["scale"], None)
+
+
+@cpu_only
+@pytest.mark.parametrize(
+    "what,over,code",
+    [c for c in BAD_PARTIAL if c[0] not in ("null partials",
+                                            "partials misaligned")],
+    ids=[c[0] for c in BAD_PARTIAL if c[0] not in ("null partials",
+                                                   "partials misaligned")])
+def test_decode_noalloc_rejects(lib, what, over, code):
+    """The allocation-free entry point validates like decode_attn (it has no
+    partials argument), before any HIP call."""
+    assert _call_noalloc(lib, _partial_args(**over)) == code
+
+
+@cpu_only
+def test_decode_noalloc_rejects_bad_out_and_oversize(lib):
+    a = _partial_args()
+    assert _call_noalloc(lib, a, out=0) == EINVAL
+    assert _call_noalloc(lib, a, out=A + 0x5000 + 4) == EALIGN
+    cap = skv.NOALLOC_SCRATCH_BYTES
+    # records of 28 heads x (4 + 128) floats per split: 1,134 splits fit
+    per_split = skv.partials_bytes(1, 28, 128, 1)
+    s_max = cap // per_split
+    assert s_max == 1134
+    assert _call_noalloc(lib, _partial_args(S=s_max + 1, T=65536)) == ESCRATCH
+    # 32 sequences of 32q hd128: 31 splits fit, 32 do not
+    big = dict(B=32, nh=32, nkvh=8, T=32768)
+    assert skv.partials_bytes(32, 32, 128, 31) <= cap < \
+        skv.partials_bytes(32, 32, 128, 32)
+    assert _call_noalloc(lib, _partial_args(S=32, **big)) == ESCRATCH
 
 
 def _call_step(lib, a, kn=A + 0x6000, vn=A + 0x7000, out=A + 0x5000):

@@ -1,0 +1,62 @@
+"""GPU: the allocation-free entry point (splitkv_decode_attn_noalloc, for
+callers that cannot allocate device memory) against splitkv_decode_attn with a
+caller records buffer, through the C ABI. Two calls in a row share the
+library's device scratch, the second with a smaller input; each output must be
+bit-identical to the existing entry point's (the same kernels), and within the
+parity bar of it.
+"""
+import numpy as np
+import pytest
+
+import synth
+from gpu_util import alloc_outputs, parity, say, to_device, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+
+def _both(case, S, blk=0):
+    import decode_attention_gqa_amd as skv
+    torch = torch_mod()
+    q, k, v, pos = to_device(case)
+    part, out_ref = alloc_outputs(case.shape, S)
+    skv.decode_attn(q, k, v, pos, part, out_ref, S, blk, case.scale)
+    out = torch.full_like(out_ref, float("nan"))
+    skv.decode_attn_noalloc(q, k, v, pos, out, S, blk, case.scale)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), out_ref.cpu().numpy()
+
+
+def test_noalloc_matches_decode_attn_two_calls():
+    import decode_attention_gqa_amd as skv
+    # first call: the headline shape at 32K rows, 128 splits (1.9 MB of
+    # records); second call: the tiny workload (4 splits, 4 KB), so that it
+    # runs over the larger call's leftover records
+    big = synth.make_case(3, synth.Shape(1, 28, 4, 128, 33024), 32768,
+                          poison_tail=True)
+    S_big, blk_big = skv.pick_splits(1, 28, 4, 128, 33024, 256)
+    say(f"noalloc call 1: 28q/4kv hd128 nkv 32768 S={S_big}")
+    got, want = _both(big, S_big, blk_big)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    parity(got, want, "noalloc call 1")
+    small = synth.make_case(1, synth.CFG1, 256, poison_tail=True)
+    say(f"noalloc call 2: 4q/2kv hd64 nkv 256 S={synth.CFG1_SPLITS}")
+    got, want = _both(small, synth.CFG1_SPLITS)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+    parity(got, want, "noalloc call 2")
+
+
+def test_noalloc_rejects_oversize_records():
+    """Records beyond the scratch: an error status, nothing enqueued."""
+    import decode_attention_gqa_amd as skv
+    torch = torch_mod()
+    case = synth.make_case(1, synth.CFG1, 256)
+    q, k, v, pos = to_device(case)
+    out = torch.zeros((1, 4, 64), device="cuda")
+    per_split = skv.partials_bytes(1, 4, 64, 1)
+    S = skv.NOALLOC_SCRATCH_BYTES // per_split + 1
+    say(f"noalloc oversize S={S}")
+    with pytest.raises(skv.SplitKVError) as e:
+        skv.decode_attn_noalloc(q, k, v, pos, out, S, 0, case.scale)
+    assert e.value.status == -5
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(out).item() == 0
