@@ -28,8 +28,11 @@ __all__ = ["SplitKVError", "load", "abi_version", "strerror", "partials_bytes",
            "decode_step", "append_kv", "workgroups_per_cu", "probe_read",
            "probe_copy", "LIB_PATH", "SUPPORTED_HEAD_DIMS", "MAX_GROUP"]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)),
-                        "libsplitkv.so")
+# SPLITKV_LIB names another build of the same library (the sanitizer build of
+# `python -m decode_attention_gqa_amd.build --sanitize`); unset, the in-tree
+# build is used.
+LIB_PATH = os.environ.get("SPLITKV_LIB") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libsplitkv.so")
 SUPPORTED_HEAD_DIMS = (8, 16, 32, 64, 128, 256)
 MAX_GROUP = 8
 ABI_VERSION = 2

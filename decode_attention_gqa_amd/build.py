@@ -1,6 +1,10 @@
 """Build libsplitkv.so (gfx950) in-tree with hipcc.
 
     python -m decode_attention_gqa_amd.build        # or build() from Python
+    python -m decode_attention_gqa_amd.build --sanitize
+        # host code under AddressSanitizer + UndefinedBehaviorSanitizer, and
+        # the C oracle likewise, into _build/sanitize/ (CPU checks only: the
+        # device code is built as usual, the sanitizers apply to host code)
 
 Every HIP source is compiled for gfx950 only. Packed-FP32 instruction
 selection is switched off for the device code (-packed-fp32-ops); the host
@@ -33,10 +37,20 @@ CFLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
           "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
-def _compile(src: str) -> tuple[str, str]:
-    obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *CFLAGS, "-Rpass-analysis=kernel-resource-usage", "-c",
-           os.path.join(CSRC, src), "-o", obj]
+# Host-side sanitizer flags: each -fsanitize goes to the host compilation only
+# (-Xarch_host), never to the gfx950 code.
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host",
+             "-fsanitize=undefined", "-Xarch_host", "-fno-sanitize-recover=all",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-g"]
+SAN_DIR = os.path.join(ROOT, "_build", "sanitize")
+CLANG = os.environ.get("CLANG", "/opt/rocm/llvm/bin/clang")
+
+
+def _compile(src: str, build_dir: str = BUILD,
+             extra: tuple = ()) -> tuple[str, str]:
+    obj = os.path.join(build_dir, os.path.splitext(src)[0] + ".o")
+    cmd = [HIPCC, *CFLAGS, *extra, "-Rpass-analysis=kernel-resource-usage",
+           "-c", os.path.join(CSRC, src), "-o", obj]
     p = subprocess.run(cmd, capture_output=True, text=True)
     if p.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{p.stderr}")
@@ -66,6 +80,57 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def asan_runtime() -> str:
+    """Path of the shared AddressSanitizer runtime of the ROCm clang (to be
+    preloaded into the Python process that loads the sanitizer builds)."""
+    p = subprocess.run([CLANG, "-print-file-name=libclang_rt.asan-x86_64.so"],
+                       capture_output=True, text=True, check=True)
+    return p.stdout.strip()
+
+
+def build_sanitized(verbose: bool = False) -> dict:
+    """libsplitkv.so and the oracle with AddressSanitizer and
+    UndefinedBehaviorSanitizer on their host code, into _build/sanitize/.
+    Returns the paths and the environment that runs the CPU checks on them:
+        SPLITKV_LIB, SPLITKV_ORACLE_LIB  the two builds
+        LD_PRELOAD                       the sanitizer runtime (prepended)
+        ASAN_OPTIONS, UBSAN_OPTIONS      abort on the first report; leak
+                                         checks off (the interpreter and
+                                         torch keep memory until exit)"""
+    os.makedirs(SAN_DIR, exist_ok=True)
+    with cf.ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 1)) as ex:
+        results = list(ex.map(lambda f: _compile(f, SAN_DIR, tuple(SAN_FLAGS)),
+                              SOURCES))
+    lib = os.path.join(SAN_DIR, "libsplitkv.so")
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC",
+           "-Xarch_host", "-fsanitize=address", "-Xarch_host",
+           "-fsanitize=undefined", "-shared-libasan", "-o", lib,
+           *[o for o, _ in results]]
+    p = subprocess.run(cmd, capture_output=True, text=True)
+    if p.returncode != 0:
+        raise RuntimeError(f"sanitizer link failed:\n{p.stderr}")
+    sys.path.insert(0, ROOT)
+    import oracle
+    olib = oracle.build(os.path.join(SAN_DIR, "liboracle.so"),
+                        ("-g", "-fno-omit-frame-pointer",
+                         "-fsanitize=address,undefined",
+                         "-fno-sanitize-recover=all", "-shared-libasan"),
+                        cc=CLANG)
+    rt = asan_runtime()
+    pre = os.environ.get("LD_PRELOAD", "")
+    env = {"SPLITKV_LIB": lib, "SPLITKV_ORACLE_LIB": olib,
+           "LD_PRELOAD": rt + (":" + pre if pre else ""),
+           "ASAN_OPTIONS": "detect_leaks=0:halt_on_error=1:abort_on_error=1",
+           "UBSAN_OPTIONS": "halt_on_error=1:print_stacktrace=1"}
+    if verbose:
+        for k, v in env.items():
+            print(f"{k}={v}")
+    return env
+
+
 if __name__ == "__main__":
-    build(verbose=True)
+    if "--sanitize" in sys.argv[1:]:
+        build_sanitized(verbose=True)
+    else:
+        build(verbose=True)
     sys.exit(0)

@@ -1,7 +1,9 @@
 // splitkv_append.hip -- KV-cache append kernel (gfx950).
 //
-// dotLLM issue #199, comment 1, section 1: every decode step first writes the
-// new K/V row(s) into the FP16 cache, and attention then reads the cache. Row
+// dotLLM issue #199, comment 1, section 1 (the cache update that comes ahead
+// of attention in a decode step): the step's freshly projected key and value
+// rows are converted to half precision and stored at their positions, and
+// only then do the attention kernels read the cache. Row
 // t of the n_rows new rows of sequence b goes to position
 //   p = positions[b] - (n_rows - 1) + t,
 // so the last new row sits at positions[b] and the live length after the

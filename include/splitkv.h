@@ -258,8 +258,7 @@ int splitkv_decode_attn_noalloc(const float *q, const uint16_t *k_cache,
                                 float scale, void *stream);
 
 /* KV-cache append, the step before attention in a decode step (dotLLM issue
- * #199, comment 1, section 1: the new K/V rows are written into the FP16
- * cache, then attention reads the cache).
+ * #199, comment 1, section 1: the cache update that precedes attention).
  *   k_new, v_new      device, fp32 [batch][n_rows][n_kv_head][head_dim],
  *                     16-byte aligned; read only.
  *   k_cache, v_cache  device, fp16 bits [batch][max_ctx][n_kv_head][head_dim],
@@ -279,8 +278,8 @@ int splitkv_append_kv(const float *k_new, const float *v_new,
                       int n_kv_head, int head_dim, int max_ctx, void *stream);
 
 /* One decode step of one layer: splitkv_append_kv with n_rows = 1, then
- * splitkv_decode_attn (dotLLM issue #199, comment 1, section 1: the new K/V
- * row goes into the FP16 cache, then attention reads the cache). For
+ * splitkv_decode_attn (dotLLM issue #199, comment 1, section 1: the cache
+ * update, then attention over the updated cache). For
  * head_dim 64/128/256 the append is folded into the partial kernel: the
  * workgroup whose split holds position positions[b] converts sequence b's
  * new row, writes it into the caches and uses the converted values for that

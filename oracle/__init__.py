@@ -14,8 +14,8 @@ cites the page passage it follows:
 * "Red Lite dev35 — long-context decode: grouped split-K attention", section
   Change (one workgroup per block and KV head, fixed block length).
 * dotLLM issue #199 (tensor-core decode attention), comment 1: section 1 (the
-  new K/V rows are written into the FP16 cache before attention) and section 2
-  (several query rows with a causal mask from positionOffset).
+  half-precision cache update ahead of attention in a decode step) and
+  section 2 (several query rows with a causal mask from positionOffset).
 """
 from __future__ import annotations
 
@@ -29,6 +29,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "oracle.c")
 _LIB = os.path.join(_HERE, "liboracle.so")
+# SPLITKV_ORACLE_LIB names a prebuilt copy (the sanitizer build); it is used
+# as is, never rebuilt.
+_ENV_LIB = os.environ.get("SPLITKV_ORACLE_LIB")
 _lock = threading.Lock()
 _lib = None
 
@@ -38,9 +41,10 @@ _u16p = np.ctypeslib.ndpointer(np.uint16, flags="C_CONTIGUOUS")
 _i32p = np.ctypeslib.ndpointer(np.int32, flags="C_CONTIGUOUS")
 
 
-def build(out_path: str = _LIB, extra_flags: tuple = ()) -> str:
-    """Compile oracle.c with gcc (no fast-math: IEEE double throughout)."""
-    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
+def build(out_path: str = _LIB, extra_flags: tuple = (),
+          cc: str = "gcc") -> str:
+    """Compile oracle.c (no fast-math: IEEE double throughout)."""
+    cmd = [cc, "-O2", "-std=c11", "-fPIC", "-shared", "-fno-fast-math",
            *extra_flags, "-o", out_path, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
     return out_path
@@ -52,8 +56,11 @@ def load(path: str | None = None):
     with _lock:
         if path is None and _lib is not None:
             return _lib
-        p = path or _LIB
-        if not os.path.exists(p) or (
+        p = path or _ENV_LIB or _LIB
+        if p == _ENV_LIB and path is None:
+            if not os.path.exists(p):
+                raise RuntimeError(f"SPLITKV_ORACLE_LIB={p} does not exist")
+        elif not os.path.exists(p) or (
                 path is None and os.path.getmtime(p) < os.path.getmtime(_SRC)):
             build(p)
         lib = ctypes.CDLL(p)

@@ -258,9 +258,9 @@ void oracle_combine(const double *records, double *out, int batch,
 
 /* ------------------------------------------------------------------------ */
 /* IEEE 754 binary32 -> binary16 with round-to-nearest, ties to even, from the
- * formats' definitions. [#199] section 1: each decode step writes the new K/V
- * row(s) into the FP16 cache before attention reads it; the conversion is
- * the standard one (the page names no other rounding).
+ * formats' definitions. [#199] section 1 (the half-precision cache update
+ * ahead of attention in a decode step) names no rounding rule, so the
+ * conversion is the standard one.
  *   - NaN stays NaN (returned as the quiet NaN 0x7E00 with the input's sign;
  *     the payload is not part of the definition);
  *   - the magnitude is rounded to a multiple of the binary16 quantum at its

@@ -1,6 +1,5 @@
-"""GPU: the KV-cache append kernel (dotLLM issue #199, comment 1, section 1:
-each decode step writes the new K/V rows into the FP16 cache, then attention
-reads it).
+"""GPU: the KV-cache append kernel (dotLLM issue #199, comment 1, section 1,
+the cache update that a decode step performs ahead of attention).
 
 The caches after an append must equal the oracle's bit for bit (NaN
 patterns compare as NaN), for every head size, rows per call and position

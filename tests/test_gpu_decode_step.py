@@ -1,8 +1,8 @@
 """GPU: one decode step with the KV-cache append folded into the partial
 kernel (splitkv_decode_step).
 
-dotLLM issue #199, comment 1, section 1: a decode step writes the new K/V
-row into the FP16 cache and attention then reads the cache. The folded form
+dotLLM issue #199, comment 1, section 1 puts the cache update ahead of
+attention within a decode step. The folded form
 must give, bit for bit, what the append kernel followed by the two-kernel
 attention gives (the caches afterwards and the output), and match the fp64
 oracle run on the oracle's own appended cache. Positions are chosen so that
