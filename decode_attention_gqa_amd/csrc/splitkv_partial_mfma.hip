@@ -220,10 +220,11 @@ __device__ __forceinline__ uint4 f16x8(const float4v &x, const float4v &y) {
                     f16x2_bits(y[0], y[1]), f16x2_bits(y[2], y[3]));
 }
 
-// Issue the loads of the 16-row tile starting at row tb (tb < hi).
+// Issue the loads of one tensor's rows of the 16-row tile starting at row tb
+// (tb < hi).
 template <int HD>
-__device__ __forceinline__ void load_tile(TileRegs<HD> &t, const uint16_t *kseq,
-                                          const uint16_t *vseq,
+__device__ __forceinline__ void load_rows(uint4 (&x)[MGeo<HD>::NL],
+                                          const uint16_t *seq,
                                           uint32_t row_bytes, uint32_t tb,
                                           uint32_t hi, uint32_t off) {
   using Geo = MGeo<HD>;
@@ -232,13 +233,20 @@ __device__ __forceinline__ void load_tile(TileRegs<HD> &t, const uint16_t *kseq,
   // every load in a loop over distinct descriptors
   tb = __builtin_amdgcn_readfirstlane(tb);
   hi = __builtin_amdgcn_readfirstlane(hi);
-  // all K first: the scores need only K, and loads return in order
 #pragma unroll
   for (int i = 0; i < Geo::NL; ++i)
-    t.k[i] = load16(rows_view(kseq, row_bytes, tb + (uint32_t)(Geo::RPI * i), hi), off);
-#pragma unroll
-  for (int i = 0; i < Geo::NL; ++i)
-    t.v[i] = load16(rows_view(vseq, row_bytes, tb + (uint32_t)(Geo::RPI * i), hi), off);
+    x[i] = load16(rows_view(seq, row_bytes, tb + (uint32_t)(Geo::RPI * i), hi), off);
+}
+
+// Issue the loads of the 16-row tile starting at row tb (tb < hi): all K
+// first (the scores need only K, and loads return in order), then V.
+template <int HD>
+__device__ __forceinline__ void load_tile(TileRegs<HD> &t, const uint16_t *kseq,
+                                          const uint16_t *vseq,
+                                          uint32_t row_bytes, uint32_t tb,
+                                          uint32_t hi, uint32_t off) {
+  load_rows<HD>(t.k, kseq, row_bytes, tb, hi, off);
+  load_rows<HD>(t.v, vseq, row_bytes, tb, hi, off);
 }
 
 // Write a loaded tile's K (or V) rows into the wave's LDS slice, row-major
@@ -266,9 +274,13 @@ __device__ __forceinline__ void stage_rows(const uint4 (&x)[MGeo<HD>::NL],
 // 8..15 (added by a DPP rotation). CB = 2: two blocks of 16 columns, block 0
 // the hi parts and block 1 the lo parts of 16 (row, head) columns (added
 // lane by lane); every product then runs twice.
-template <int HD, bool SAFE, int CB>
+// after_k / after_v run right after the tile's K / V rows have been staged
+// (their registers are free from then on): the loop uses them to issue the
+// next tile's loads early where that measured faster.
+template <int HD, bool SAFE, int CB, typename AfterK, typename AfterV>
 __device__ __forceinline__ void compute_tile(
-    const TileRegs<HD> &t, unsigned char *slice, uint32_t tb,
+    TileRegs<HD> &t, AfterK after_k, AfterV after_v, unsigned char *slice,
+    uint32_t tb,
     uint32_t mask_from, uint32_t lim, const half8 (&qf)[CB][MGeo<HD>::KS],
     float4v (&oacc)[CB][MGeo<HD>::DB], float &m_run, float &m_true,
     float &s_run, int col, int grp, int lane, bool hi_col) {
@@ -280,20 +292,28 @@ __device__ __forceinline__ void compute_tile(
   __builtin_amdgcn_s_setprio(2);
   // a4: scores S = K · Q'ᵀ, K operands read back from the staged rows.
   stage_rows<HD, Geo::KSTR>(t.k, slice, lane);
+  after_k(t);
   uint4 ka[Geo::KS];
 #pragma unroll
   for (int ks = 0; ks < Geo::KS; ++ks)
     ka[ks] = *reinterpret_cast<const uint4 *>(slice + col * Geo::KSTR +
                                                64 * ks + 16 * grp);
+  // two accumulators (even and odd k-steps) halve the dependent MFMA chain
+  // (28 layers at 32K rows: partial kernel 13.15 against 13.3 us)
   float4v sc[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) {
-    sc[cb] = float4v{0.f, 0.f, 0.f, 0.f};
+    float4v s0 = float4v{0.f, 0.f, 0.f, 0.f};
+    float4v s1 = float4v{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < Geo::KS; ++ks)
-      sc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(ka[ks]),
-                                                      qf[cb][ks], sc[cb], 0,
-                                                      0, 0);
+    for (int ks = 0; ks < Geo::KS; ks += 2) {
+      s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(ka[ks]),
+                                                  qf[cb][ks], s0, 0, 0, 0);
+      if (ks + 1 < Geo::KS)
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+            as_half8(ka[ks + 1]), qf[cb][ks + 1], s1, 0, 0, 0);
+    }
+    sc[cb] = s0 + s1;
   }
   // hi + lo columns; rows at or past the column's end (last tiles only) score
   // -inf.
@@ -356,6 +376,7 @@ __device__ __forceinline__ void compute_tile(
   // O += Vᵀ · P: lane (grp, col) reads dim 16b + col of rows 4*grp + 0..3,
   // the same row order as its p values.
   stage_rows<HD, Geo::VSTR>(t.v, vlds, lane);
+  after_v(t);
   const int c4 = col >> 2;
   const int cm = col & 3;
 #pragma unroll
@@ -640,21 +661,33 @@ partial_mfma_kernel(PartialArgs a) {
     // through LDS), then issue the next tile's loads (only tiles with rows:
     // even loads past the record limit, which return zeros without touching
     // memory, cost address-unit time). Each wave has at most one tile in
-    // flight, and none while it computes: at 32K rows, issuing the next tile
-    // before computing the current one (one more tile in flight per wave)
-    // measured 0.4 us per layer slower, and a second register tile 0.6 us,
-    // because deeper memory queues serve the workgroups dispatched last later
-    // still.
+    // flight: at 32K rows, issuing the next tile before computing the current
+    // one (one more tile in flight per wave) measured 0.4 us per layer
+    // slower, a second register tile 0.6 us, and issuing the next tile's K
+    // and V as soon as the current ones are staged 0.15 us, because deeper
+    // memory queues serve the workgroups dispatched last later still. At
+    // head_dim 256 (few tiles per wave, each computed for longer) the early
+    // issue measured faster (8,400 rows: 7.80 against 7.99 us).
+    constexpr bool kEarly = HD >= 256;
     while (true) {
       if constexpr (FOLD) {
         if (t0 == app_tb) put_new_row(tr);
       }
-      compute_tile<HD, (R > 1), CB>(tr, slice, t0, mask32, lim32, qf, oacc,
-                                    m_run, m_true, s_run, col, grp, lane,
-                                    hi_col);
-      t0 += step;
-      if (t0 >= hi32) break;
-      load_tile<HD>(tr, kseq, vseq, row_bytes, t0, hi32, off);
+      const uint32_t nt = t0 + step;
+      const bool more = nt < hi32;
+      compute_tile<HD, (R > 1), CB>(
+          tr,
+          [&](TileRegs<HD> &x) {
+            if (kEarly && more) load_rows<HD>(x.k, kseq, row_bytes, nt, hi32, off);
+          },
+          [&](TileRegs<HD> &x) {
+            if (kEarly && more) load_rows<HD>(x.v, vseq, row_bytes, nt, hi32, off);
+          },
+          slice, t0, mask32, lim32, qf, oacc, m_run, m_true, s_run, col, grp,
+          lane, hi_col);
+      t0 = nt;
+      if (!more) break;
+      if constexpr (!kEarly) load_tile<HD>(tr, kseq, vseq, row_bytes, t0, hi32, off);
     }
   } else {
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
