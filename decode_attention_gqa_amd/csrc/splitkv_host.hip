@@ -194,16 +194,18 @@ int splitkv_workgroups_per_cu(int head_dim, int group) {
   if (!splitkv::head_dim_supported(head_dim) || group < 1 ||
       group > splitkv::kMaxGroup)
     return 0;
-  // From the compiler's resource report of each instantiation (waves per
-  // SIMD with one wave of the workgroup on each SIMD); a build check keeps
-  // this table equal to the report.
+  // From the compiler's resource report of each instantiation: waves per
+  // SIMD x 4 SIMDs / waves per workgroup, and no more than the LDS of a
+  // compute unit holds (160 KiB; the head_dim-256 kernel runs 8-wave
+  // workgroups of 143 KB: one per unit); a build check keeps this table
+  // equal to the report.
   switch (head_dim) {
     case 8: { static const int t[8] = {4, 4, 3, 3, 2, 2, 2, 2}; return t[group - 1]; }
     case 16: { static const int t[8] = {4, 3, 3, 2, 2, 2, 2, 1}; return t[group - 1]; }
     case 32: { static const int t[8] = {4, 3, 3, 2, 2, 2, 2, 1}; return t[group - 1]; }
     case 64: return 7;
     case 128: return 4;
-    case 256: return 2;
+    case 256: return 1;
     default: return 0;
   }
 }

@@ -2,7 +2,8 @@
 // attention for gfx950 (CDNA4), matrix-core form, used for head_dim 64, 128
 // and 256.
 //
-// Same contract as the vector-ALU kernel: one workgroup (4 waves) per (split,
+// Same contract as the vector-ALU kernel: one workgroup (4 waves; 8 at
+// head_dim 256) per (split,
 // KV head, sequence) on a static grid dim3(n_splits, n_kv_head, batch), the
 // live length read from positions[] on the device ("10 · R4 — decode
 // split-attention dim-parallel rewrite", section 2.2), all G query heads of
@@ -33,7 +34,7 @@
 // Start of a workgroup: the live length is read first and wave 0 issues the
 // query loads while it is in flight (they do not depend on it), every wave
 // then issues its first tile's loads, wave 0 converts the queries into the
-// MFMA operand once and the waves read it from LDS after one barrier. End: the four waves' states
+// MFMA operand once and the waves read it from LDS after one barrier. End: the waves' states
 // are merged through LDS into one record per query head; a split of at most
 // one tile has rows only in wave 0, which writes the records itself.
 //
@@ -71,8 +72,6 @@ namespace {
 
 using detail::dpp_mov;
 using detail::fast_exp2;
-using detail::kThreads;
-using detail::kWaves;
 using detail::neg_inf;
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -100,6 +99,19 @@ struct MGeo {
   // hold the wave's unnormalised output for the workgroup merge.
   static constexpr int SLICE = KTILE + kTileRows * VSTR;
   static_assert(HD % 32 == 0 && HD <= 256, "head_dim");
+};
+
+// Waves per workgroup: 4 (one per SIMD), 8 at head_dim 256. A head_dim-256
+// tile is computed for longer and a split holds few tiles (8,400 rows over 96
+// to 128 splits: 5-6 tiles), so with 4 waves some waves take a second tile
+// after their first; 8 waves put every tile of a split of up to 128 rows in
+// the first round (16q/2kv at 8,400 rows: 7.23 against 7.39 us at 96 splits,
+// 7.60 against 7.84 at 128). The 8-wave workgroup uses 143 KB of LDS, so one
+// fits a compute unit.
+template <int HD>
+struct MWaves {
+  static constexpr int W = HD >= 256 ? 8 : 4;
+  static constexpr int kThr = 64 * W;
 };
 
 // One tile's K and V rows as loaded: load i holds rows RPI*i + lane / LPR,
@@ -417,9 +429,11 @@ __device__ __forceinline__ float hilo_sum(const float4v (&oacc)[CB][DB], int i,
 // row, grouped); a separate instantiation, so that the plain forms keep
 // their register count.
 template <int HD, int G, bool PER_HEAD = false, int R = 1, bool FOLD = false>
-__global__ __launch_bounds__(kThreads, 2) void
+__global__ __launch_bounds__(MWaves<HD>::kThr, MWaves<HD>::W == 8 ? 1 : 2) void
 partial_mfma_kernel(PartialArgs a) {
   using Geo = MGeo<HD>;
+  constexpr int kW = MWaves<HD>::W;       // waves per workgroup
+  constexpr int kT = MWaves<HD>::kThr;    // threads per workgroup
   constexpr int SLICE = Geo::SLICE;
   constexpr int NC = G * R;                          // (row, head) columns
   // one 16-column block holds 8 columns (hi and lo parts), two hold 16
@@ -462,9 +476,9 @@ partial_mfma_kernel(PartialArgs a) {
   const int grp = lane >> 4;
   const bool hi_col = col < 8;   // (one column block) hi part of a column
 
-  __shared__ __attribute__((aligned(16))) unsigned char sm_v[kWaves * SLICE];
+  __shared__ __attribute__((aligned(16))) unsigned char sm_v[kW * SLICE];
   // each wave's state per column: (reference max, exact max, sum, unused)
-  __shared__ float4 sm_st[kWaves][NC];
+  __shared__ float4 sm_st[kW][NC];
   // the query operand, converted once per workgroup (lane-major per ks)
   __shared__ half8 sm_q[CB][Geo::KS][64];
   // a column's output in the wave's slice: HD floats, padded (16 floats, 4
@@ -536,7 +550,7 @@ partial_mfma_kernel(PartialArgs a) {
   const uint32_t hi32 = (uint32_t)hi;
   const uint32_t mask32 = (uint32_t)mask_from;
   const uint32_t lim32 = (uint32_t)col_end;
-  const uint32_t step = (uint32_t)(kWaves * kTileRows);
+  const uint32_t step = (uint32_t)(kW * kTileRows);
   uint32_t t0 = (uint32_t)lo + (uint32_t)(wave * kTileRows);
   if (lo >= hi) t0 = hi32;  // idle split
 
@@ -551,7 +565,7 @@ partial_mfma_kernel(PartialArgs a) {
     if (a.k_new != nullptr && pos_b >= 0 && pos_b < a.max_ctx &&
         (long long)pos_b >= lo && (long long)pos_b < hi) {
       const uint32_t j = ((uint32_t)pos_b - (uint32_t)lo) / kTileRows;
-      if ((int)(j % kWaves) == wave) {
+      if ((int)(j % kW) == wave) {
         app_tb = (uint32_t)lo + j * kTileRows;
         const size_t src =
             ((size_t)b * a.n_kv_head + hk) * HD + 8 * (lane % Geo::LPR);
@@ -694,10 +708,10 @@ partial_mfma_kernel(PartialArgs a) {
     lds_barrier();
   }
 
-  // a6: merge the four waves and write the records. Each wave puts its state
+  // a6: merge the waves and write the records. Each wave puts its state
   // in LDS (reference max, exact max and sum per head; O with the hi and lo
   // columns added), then after one barrier every thread merges one float4 of
-  // one head's output over the four waves with weights exp2(m_ref - m_all),
+  // one head's output over the waves with weights exp2(m_ref - m_all),
   // m_all the largest exact max: the record is relative to the exact max.
   // This runs after the workgroup's last data has landed, so its latency is
   // on the kernel's critical path: all of a thread's LDS reads are issued
@@ -757,26 +771,26 @@ partial_mfma_kernel(PartialArgs a) {
           make_float4(o4[0], o4[1], o4[2], o4[3]);
   }
   __syncthreads();
-  for (int idx = tid; idx < NC * D4; idx += kThreads) {
+  for (int idx = tid; idx < NC * D4; idx += kT) {
     const int gg = idx / D4;
     const int d4 = idx % D4;
     // column gg = (row r, head g); rows past n_q have no record
     const int r = gg / G;
     if (R > 1 && rs.t + r >= a.n_q) continue;
-    float4 stw[kWaves], x[kWaves];
+    float4 stw[kW], x[kW];
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < kW; ++w) {
       stw[w] = sm_st[w][gg];
       x[w] = *reinterpret_cast<const float4 *>(sm_v + w * SLICE + gg * OSTR +
                                                16 * d4);
     }
     float mm = neg_inf();
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, stw[w].y);
+    for (int w = 0; w < kW; ++w) mm = fmaxf(mm, stw[w].y);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float st = 0.0f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < kW; ++w) {
       const float mw = stw[w].x;
       const float c = (mw == neg_inf()) ? 0.0f : fast_exp2(mw - mm);
       acc.x = fmaf(c, x[w].x, acc.x);
@@ -814,12 +828,12 @@ template <int HD, int G>
 hipError_t launch_one(const PartialArgs &a, int batch, hipStream_t stream) {
   if (a.k_new != nullptr) {
     hipLaunchKernelGGL((partial_mfma_kernel<HD, G, false, 1, true>),
-                       dim3(a.n_splits, a.n_kv_head, batch), dim3(kThreads),
+                       dim3(a.n_splits, a.n_kv_head, batch), dim3(MWaves<HD>::kThr),
                        0, stream, a);
   } else {
     dim3 grid;
     const PartialArgs b = with_row_grid(a, a.n_q, batch, grid);
-    hipLaunchKernelGGL((partial_mfma_kernel<HD, G>), grid, dim3(kThreads), 0,
+    hipLaunchKernelGGL((partial_mfma_kernel<HD, G>), grid, dim3(MWaves<HD>::kThr), 0,
                        stream, b);
   }
   return hipGetLastError();
@@ -846,7 +860,7 @@ hipError_t launch_rows(const PartialArgs &a, int batch, hipStream_t stream) {
   dim3 grid;
   const PartialArgs b = with_row_grid(a, (a.n_q + R - 1) / R, batch, grid);
   hipLaunchKernelGGL((partial_mfma_kernel<HD, G, false, R>), grid,
-                     dim3(kThreads), 0, stream, b);
+                     dim3(MWaves<HD>::kThr), 0, stream, b);
   return hipGetLastError();
 }
 
@@ -882,7 +896,7 @@ hipError_t launch_rows_hd(int group, int rows, const PartialArgs &a,
 template <int HD>
 hipError_t launch_per_head(const PartialArgs &a, int batch, hipStream_t stream) {
   hipLaunchKernelGGL((partial_mfma_kernel<HD, 1, true>),
-                     dim3(a.n_splits, a.n_head, batch), dim3(kThreads), 0,
+                     dim3(a.n_splits, a.n_head, batch), dim3(MWaves<HD>::kThr), 0,
                      stream, a);
   return hipGetLastError();
 }

@@ -111,8 +111,9 @@ size_t splitkv_partials_bytes(int batch, int n_head, int head_dim,
 /* Partial-kernel workgroups that can be resident on one compute unit at
  * once for (head_dim, group = n_head / n_kv_head), as the compiler's
  * register and LDS allocation of that kernel instantiation allows (a
- * workgroup is 4 waves, one per SIMD). Used by the split heuristic to size
- * one full round of workgroups. Returns 0 for an unsupported pair. */
+ * workgroup is 4 waves, one per SIMD; 8 waves at head_dim 256). Used by the
+ * split heuristic to size one full round of workgroups. Returns 0 for an
+ * unsupported pair. */
 int splitkv_workgroups_per_cu(int head_dim, int group);
 
 /* Split heuristic: chooses n_splits (and block_len, 0 = ceil rule) for a
