@@ -112,6 +112,13 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   const float *base =
       a.partials + ((size_t)b * a.n_splits * a.n_head + h) * pstr;
   const int dofs = 4 + d_base + 4 * c;
+  // The records of this (sequence, head) through one raw buffer view based
+  // at its first record: the per-record offsets are 32-bit (the host keeps a
+  // sequence's records below 2 GiB), with no 64-bit address arithmetic per
+  // load (28q hd128 at 32K rows, 128 splits: 3.21 against 3.28-3.33 us).
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+  const uint32_t rbytes = (uint32_t)(rstride * sizeof(float));
 
   float m = neg_inf(), s = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -124,9 +131,16 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
       hdr[u] = make_float2(neg_inf(), 0.0f);
       oc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (sp < a.n_splits) {
-        const float *r = base + (size_t)sp * rstride;
-        hdr[u] = *reinterpret_cast<const float2 *>(r);
-        oc[u] = *reinterpret_cast<const float4 *>(r + dofs);
+        const uint32_t ro = (uint32_t)sp * rbytes;
+        const auto h2 = __builtin_amdgcn_raw_buffer_load_b64(rb, (int)ro, 0, 0);
+        const auto o4 = __builtin_amdgcn_raw_buffer_load_b128(
+            rb, (int)(ro + 4u * (uint32_t)dofs), 0, 0);
+        hdr[u] = make_float2(__builtin_bit_cast(float, (unsigned)h2[0]),
+                             __builtin_bit_cast(float, (unsigned)h2[1]));
+        oc[u] = make_float4(__builtin_bit_cast(float, (unsigned)o4[0]),
+                            __builtin_bit_cast(float, (unsigned)o4[1]),
+                            __builtin_bit_cast(float, (unsigned)o4[2]),
+                            __builtin_bit_cast(float, (unsigned)o4[3]));
       }
     }
     float mn = m;

@@ -63,6 +63,9 @@ int check_combine_shape(int batch, int n_head, int head_dim, int n_splits) {
   if (!splitkv::head_dim_supported(head_dim)) return SPLITKV_EUNSUPPORTED;
   if (n_splits > kMaxSplits || n_head > kMaxGridYZ || batch > kMaxGridYZ)
     return SPLITKV_EINVAL;
+  // The combine addresses one sequence's records with 32-bit byte offsets.
+  if ((long long)n_splits * n_head * (4 + head_dim) * 4 > (long long)INT_MAX)
+    return SPLITKV_EINVAL;
   return SPLITKV_OK;
 }
 

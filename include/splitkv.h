@@ -71,7 +71,8 @@
  * Supported shapes: head_dim in {8, 16, 32, 64, 128, 256}; G = n_head /
  * n_kv_head in 1..8; n_splits in 1..65535; n_kv_head and batch <= 65535;
  * max_ctx + n_splits < 2^31; (max_ctx + 64) * n_kv_head * head_dim * 2 bytes
- * (a sequence's K or V cache plus one tile) below 4 GiB.
+ * (a sequence's K or V cache plus one tile) below 4 GiB; n_splits * n_head *
+ * (4 + head_dim) * 4 bytes (a sequence's split records) below 2 GiB.
  */
 #ifndef SPLITKV_H
 #define SPLITKV_H

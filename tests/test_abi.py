@@ -294,6 +294,7 @@ BAD_COMBINE = [
     ("head_dim 48", (A, A + 0x100, 1, 28, 48, 32), EUNSUP),
     ("partials misaligned", (A + 4, A + 0x100, 1, 28, 128, 32), EALIGN),
     ("out misaligned", (A, A + 0x104, 1, 28, 128, 32), EALIGN),
+    ("sequence records >= 2 GiB", (A, A + 0x100, 1, 8192, 256, 1024), EINVAL),
 ]
 
 
