@@ -34,6 +34,9 @@ Usage: python bench.py [--steps K] [--warmup W] [--nkv N] [--layers L]
        python bench.py --mode rows      # n_q query rows per sequence (causal)
        python bench.py --mode long      # 28q/4kv hd128 at 16K..128K rows
        python bench.py --mode batch     # the same shape, 1..8 sequences at 16K/32K
+       python bench.py --mode profile --workload growing|7b2k|hd256|ragged
+                                        # one configuration's partial and
+                                        # combine launches, for rocprofv3
        python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --kernels-json F
                                         # fold two rocprofv3 --pmc runs
 """
@@ -62,6 +65,7 @@ CSRC = os.path.join(ROOT, "decode_attention_gqa_amd", "csrc")
 PARTIAL_SRCS = [os.path.join(CSRC, f) for f in (
     "splitkv_partial.hip", "splitkv_partial_mfma.hip",
     "splitkv_partial_common.h")]
+COMBINE_SRCS = [os.path.join(CSRC, "splitkv_combine.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "partial_hd128_g7_traffic.json")
 
 
@@ -490,6 +494,99 @@ def run_kernels(args):
                       "copy_bytes": nbytes,
                       "kv_bytes_per_partial": synth.kv_bytes(4, 128, args.nkv),
                       "partial_src_sha256_16": source_hash()}), flush=True)
+
+
+def run_profile(args):
+    """Profiler workload for one configuration (`--workload`): graphs of its
+    partial-kernel launches and of its combine launches at the heuristic's
+    split count over the layers' separate buffers (HIP-event timed), then a
+    plain copy of known size (the counter scale). rocprofv3 --kernel-trace
+    --stats and the FETCH_SIZE / WRITE_SIZE passes run on this mode; one JSON
+    line carries what --summarize-pmc needs to turn counters into bytes."""
+    import numpy as np
+    import torch
+
+    import decode_attention_gqa_amd as skv
+    import synth
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    w = args.workload
+    if w == "growing":
+        sh, layers, nkv = synth.CFG3, args.layers, args.nkv
+        case = synth.make_offset_case(3, sh, sh.max_ctx)
+        case.positions[:] = nkv - 1
+        name = f"28q/4kv hd128, nkv {nkv} (max_ctx {sh.max_ctx}), {layers} layers"
+    elif w == "7b2k":
+        sh, layers, nkv = synth.CFG2, synth.CFG2_LAYERS, synth.CFG2.max_ctx
+        case = synth.make_case(2, sh, nkv)
+        name = f"7B 28q/4kv hd128, nkv {nkv}, {layers} layers"
+    elif w == "hd256":
+        sh, layers, nkv = synth.CFG4, synth.CFG4_LAYERS, synth.CFG4_NKV
+        case = synth.make_case(4, sh, nkv)
+        name = f"16q/2kv hd256, nkv {nkv}, {layers} layers"
+    elif w == "ragged":
+        sh, layers = synth.CFG5, 1
+        lengths = synth.cfg5_lengths()
+        nkv = int(lengths.sum())
+        # values do not affect timing: K/V drawn on the GPU below
+        q = synth.make_q(5, 0, sh)
+        case = synth.Case(sh, q, np.zeros((sh.batch, 1, sh.n_kv_head,
+                                            sh.head_dim), np.float16),
+                          None, (lengths - 1).astype(np.int32), sh.scale)
+        name = (f"32 x 32q/8kv hd128, lengths U{{512..32768}} "
+                f"(total {nkv} rows), 1 layer")
+    else:
+        raise SystemExit(f"unknown workload {w}")
+    S, blk = skv.pick_splits(sh.batch, sh.n_head, sh.n_kv_head, sh.head_dim,
+                             sh.max_ctx, cu)
+    if w == "ragged":
+        dev = torch.device("cuda", 0)
+        g = torch.Generator(device=dev)
+        g.manual_seed(5)
+
+        class _L:
+            pass
+        lay = _L()
+        lay.L = 1
+        kk = torch.randn((sh.batch, sh.max_ctx, sh.n_kv_head, sh.head_dim),
+                         generator=g, device=dev, dtype=torch.float16)
+        vv = torch.randn(kk.shape, generator=g, device=dev,
+                         dtype=torch.float16)
+        qq = torch.from_numpy(case.q).to(dev)
+        pos = torch.from_numpy(case.positions).to(dev)
+        part = torch.empty(skv.partials_bytes(sh.batch, sh.n_head, sh.head_dim,
+                                              S) // 4, device=dev)
+        out = torch.empty((sh.batch, sh.n_head, sh.head_dim), device=dev)
+        lay.partial = lambda l: skv.partial(qq, kk, vv, pos, part, S, blk,
+                                            sh.scale)
+        lay.combine = lambda l: skv.combine(part, out, S)
+        kv = synth.kv_bytes(sh.n_kv_head, sh.head_dim, lengths)
+    else:
+        lay = Layers(layers, sh.max_ctx, S, blk, sh, case)
+        kv = synth.kv_bytes(sh.n_kv_head, sh.head_dim, case.nkv)
+    reps = args.kernel_reps
+    p_mean, p_best = time_kernel(torch, lay.partial, lay.L, reps)
+    c_mean, c_best = time_kernel(torch, lay.combine, lay.L, reps)
+    nbytes = args.copy_mib << 20
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    skv.probe_copy(src, dst, cu * 16)
+    torch.cuda.synchronize()
+    rec = skv.partials_bytes(sh.batch, sh.n_head, sh.head_dim, S)
+    print(json.dumps({
+        "mode": "profile", "workload": w, "description": name,
+        "nkv": nkv, "n_splits": S, "block_len": blk, "layers": lay.L,
+        # time_kernel: L eager launches, then a graph of `reps` launches
+        # replayed 6 times
+        "partial_launches": lay.L + 6 * reps,
+        "combine_launches": lay.L + 6 * reps,
+        "partial_avg_us_events": round(p_mean * 1e3, 3),
+        "partial_best_us_events": round(p_best * 1e3, 3),
+        "combine_avg_us_events": round(c_mean * 1e3, 3),
+        "kv_bytes_per_partial": kv,
+        "partial_gbps_events": round(kv / (p_mean * 1e-3) / 1e9, 1),
+        "record_bytes": rec, "copy_bytes": nbytes,
+        "partial_src_sha256_16": source_hash(),
+        "combine_src_sha256_16": source_hash(COMBINE_SRCS)}), flush=True)
 
 
 def run_ragged(args):
@@ -978,10 +1075,15 @@ def summarize_pmc(fetch_dir: str, write_dir: str, copy_bytes: int,
         with open(kernels_json) as f:
             meta = json.loads(f.read().strip().splitlines()[-1])
         for k in ("nkv", "n_splits", "block_len", "kv_bytes_per_partial",
-                  "partial_src_sha256_16"):
-            res[k] = meta[k]
+                  "partial_src_sha256_16", "workload", "record_bytes",
+                  "combine_src_sha256_16"):
+            if k in meta:
+                res[k] = meta[k]
         res["fetch_over_algorithmic"] = round(
             res["partial_fetch_bytes"] / meta["kv_bytes_per_partial"], 4)
+        if "record_bytes" in meta:
+            res["combine_fetch_over_records"] = round(
+                res["combine_fetch_bytes"] / meta["record_bytes"], 4)
     print(json.dumps(res, indent=1))
     if out_path:
         with open(out_path, "w") as f:
@@ -1014,7 +1116,7 @@ def main():
     ap.add_argument("--write-traffic", default=None)
     ap.add_argument("--mode", choices=["main", "kernels", "ragged", "configs",
                                        "oracle", "step", "per_head", "rows",
-                                       "long", "batch"],
+                                       "long", "batch", "profile"],
                     default="main")
     ap.add_argument("--ragged-batch", type=int, default=32)
     ap.add_argument("--batches", type=int, nargs="*", default=[1, 2, 4, 8],
@@ -1036,6 +1138,9 @@ def main():
     ap.add_argument("--ragged-full", action="store_true",
                     help="every sequence at full length (uniform batch)")
     ap.add_argument("--copy-mib", type=int, default=256)
+    ap.add_argument("--workload", default="growing",
+                    choices=["growing", "7b2k", "hd256", "ragged"],
+                    help="--mode profile: which configuration")
     args = ap.parse_args()
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1],
@@ -1048,6 +1153,8 @@ def main():
         return 2
     if args.sweep:
         run_sweep(args)
+    elif args.mode == "profile":
+        run_profile(args)
     elif args.mode == "kernels":
         run_kernels(args)
     elif args.mode == "ragged":
