@@ -74,10 +74,17 @@ def log(*a):
 
 
 def source_hash(paths=PARTIAL_SRCS) -> str:
+    """Hash of the kernel sources' code: comments and whitespace are removed
+    first, so that editing a comment does not mark counters taken on the
+    same code as stale."""
+    import re
     h = hashlib.sha256()
     for p in paths:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -3,9 +3,9 @@
 // and 256.
 //
 // Same contract as the vector-ALU kernel: one workgroup (4 waves; 8 at
-// head_dim 256) per (split,
-// KV head, sequence) on a static grid dim3(n_splits, n_kv_head, batch), the
-// live length read from positions[] on the device ("10 · R4 — decode
+// head_dim 256) per (split, KV head, sequence) on a static grid
+// dim3(n_splits, n_kv_head, batch), the live length read from positions[] on
+// the device ("10 · R4 — decode
 // split-attention dim-parallel rewrite", section 2.2), all G query heads of
 // the KV head served by one read of each K/V row ("Red Lite dev35 —
 // long-context decode: grouped split-K attention", Change), online softmax per
@@ -18,8 +18,8 @@
 // reductions, which measured at about 78 wave instructions per KV row for
 // 28q/4kv hd128 (the VALU issue limit lands near half of the HBM rate). On
 // the matrix cores they take one v_mfma_f32_16x16x32_f16 per 16 rows and 32
-// dims (scores) and one v_mfma_f32_16x16x16_f16 per 16 rows and 16 dims
-// (output).
+// dims (scores, accumulated in two chains of even and odd 32-dim steps) and
+// one v_mfma_f32_16x16x16_f16 per 16 rows and 16 dims (output).
 //
 // Precision: the MFMA takes fp16 operands and accumulates in fp32. K and V
 // are fp16 already. q (scaled by scale*log2(e)) and the softmax weights p are
@@ -34,9 +34,10 @@
 // Start of a workgroup: the live length is read first and wave 0 issues the
 // query loads while it is in flight (they do not depend on it), every wave
 // then issues its first tile's loads, wave 0 converts the queries into the
-// MFMA operand once and the waves read it from LDS after one barrier. End: the waves' states
-// are merged through LDS into one record per query head; a split of at most
-// one tile has rows only in wave 0, which writes the records itself.
+// MFMA operand once and the waves read it from LDS after one barrier. End:
+// the waves' states are merged through LDS into one record per query head; a
+// split of at most one tile has rows only in wave 0, which writes the records
+// itself.
 //
 // Data flow of one wave over a tile of 16 rows (a workgroup's waves take
 // interleaved tiles):
@@ -49,7 +50,9 @@
 //      wave's LDS slice; the next tile's loads are issued into the same
 //      registers once the staged tile is computed (one tile per wave in
 //      flight at most: fewer bytes queued in the memory system measured
-//      faster than keeping every wave's next tile in flight).
+//      faster than keeping every wave's next tile in flight). At head_dim 256
+//      the next tile's K (V) loads leave as soon as the current K (V) is
+//      staged.
 //   K: LDS rows 16 bytes past a multiple of 256 bytes apart, so the 16 rows
 //      of an operand read fall in 16 different bank groups; read back as the
 //      A operand of S = K·Q'ᵀ: lane l holds row l % 16, dims 32*ks + 8*(l/16);
