@@ -680,11 +680,18 @@ partial_mfma_kernel(PartialArgs a) {
     // memory, cost address-unit time). Each wave has at most one tile in
     // flight: at 32K rows, issuing the next tile before computing the current
     // one (one more tile in flight per wave) measured 0.4 us per layer
-    // slower, a second register tile 0.6 us, and issuing the next tile's K
-    // and V as soon as the current ones are staged 0.15 us, because deeper
-    // memory queues serve the workgroups dispatched last later still. At
-    // head_dim 256 (few tiles per wave, each computed for longer) the early
-    // issue measured faster (8,400 rows: 7.80 against 7.99 us).
+    // slower and a second register tile 0.6 us, because deeper memory queues
+    // serve the workgroups dispatched last later still; issuing the next
+    // tile's K and V as soon as the current ones are staged (in a separate
+    // code path, so that the load counters are exact) is within 0.1 us either
+    // way at 2K-32K rows, and issuing only the second tile early is 0.3 us
+    // slower at 16K and 32K. At head_dim 256 (few tiles per wave, each
+    // computed for longer) the early issue measured faster (8,400 rows: 7.80
+    // against 7.99 us). Written as below, with one path for both cases, the
+    // compiler's counters make the V stage wait for the next tile's K loads
+    // as well; the two-path form with exact counts was slower there (254
+    // against 199 VGPRs; partial kernel 7.85 against 7.51 us at 8,400 rows,
+    // 14.4 against 14.2 us at 32K).
     constexpr bool kEarly = HD >= 256;
     while (true) {
       if constexpr (FOLD) {
