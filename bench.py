@@ -39,6 +39,9 @@ Usage: python bench.py [--steps K] [--warmup W] [--nkv N] [--layers L]
                                         # combine launches, for rocprofv3
        python bench.py --summarize-pmc FETCH_DIR WRITE_DIR --kernels-json F
                                         # fold two rocprofv3 --pmc runs
+       python bench.py --summarize-trace TRACE_DIR
+                                        # per-layer partial / gap / combine
+                                        # split of a --kernel-trace run
 """
 from __future__ import annotations
 
@@ -1098,6 +1101,68 @@ def summarize_pmc(fetch_dir: str, write_dir: str, copy_bytes: int,
             f.write("\n")
 
 
+def summarize_trace(trace_dir: str, layers: int, out_path: str | None):
+    """Per-layer split of the layer graphs from a rocprofv3 --kernel-trace run
+    of the default mode. The dispatches are sorted by start time; runs of
+    alternating partial / combine dispatches are cut into replays of `layers`
+    layers. Per layer: the partial kernel's duration, the gap to the
+    combine's start, the combine's duration, the gap to the next layer's
+    partial kernel, and the period from one partial start to the next
+    (medians over all replays). The tracer stamps a dispatch that waits for
+    the one before it as starting when that one ends, so the time between
+    two kernels is counted in the second one's duration here."""
+    rows = []
+    for path in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"),
+                          recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                name = r["Kernel_Name"]
+                kind = ("P" if "partial_" in name else
+                        "C" if "combine_kernel" in name else "X")
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]),
+                             kind))
+    rows.sort()
+    runs, cur = [], []
+    for st, en, kind in rows:
+        expect = "P" if len(cur) % 2 == 0 else "C"
+        if kind != expect:
+            runs.append(cur)
+            cur = []
+            if kind != "P":
+                continue
+        cur.append((st, en, kind))
+    runs.append(cur)
+    n = 2 * layers
+    replays = [r[i:i + n] for r in runs for i in range(0, len(r) - n + 1, n)]
+    if not replays:
+        raise SystemExit(f"no layer-graph replays found under {trace_dir}")
+    pd, cd, gpc, gcp, per = [], [], [], [], []
+    for r in replays:
+        for i in range(0, n, 2):
+            (ps, pe, _), (cs, ce, _) = r[i], r[i + 1]
+            pd.append(pe - ps)
+            cd.append(ce - cs)
+            gpc.append(cs - pe)
+            if i + 2 < n:
+                gcp.append(r[i + 2][0] - ce)
+                per.append(r[i + 2][0] - ps)
+
+    def med(x):
+        return round(statistics.median(x) / 1e3, 3)
+
+    res = {"replays": len(replays), "layers": layers,
+           "partial_us": med(pd), "gap_partial_to_combine_us": med(gpc),
+           "combine_us": med(cd), "gap_combine_to_partial_us": med(gcp),
+           "layer_period_us": med(per),
+           "replay_us_per_layer": round(statistics.median(
+               [(r[-1][1] - r[0][0]) / layers for r in replays]) / 1e3, 3)}
+    print(json.dumps(res, indent=1))
+    if out_path:
+        with open(out_path, "w") as f:
+            json.dump(res, f, indent=1)
+            f.write("\n")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -1119,6 +1184,9 @@ def main():
     ap.add_argument("--sweep-blocks", type=int, nargs="*", default=[128, 256, 512])
     ap.add_argument("--summarize-pmc", nargs=2, default=None,
                     metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--summarize-trace", default=None, metavar="TRACE_DIR",
+                    help="per-layer partial / gap / combine split of the layer "
+                         "graphs in a rocprofv3 --kernel-trace run")
     ap.add_argument("--kernels-json", default=None)
     ap.add_argument("--write-traffic", default=None)
     ap.add_argument("--mode", choices=["main", "kernels", "ragged", "configs",
@@ -1149,6 +1217,9 @@ def main():
                     choices=["growing", "7b2k", "hd256", "ragged"],
                     help="--mode profile: which configuration")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace, args.layers, args.write_traffic)
+        return 0
     if args.summarize_pmc:
         summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1],
                       args.copy_mib << 20, args.kernels_json, args.write_traffic)
