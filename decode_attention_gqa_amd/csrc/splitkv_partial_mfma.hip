@@ -279,9 +279,81 @@ __device__ __forceinline__ void stage_rows(const uint4 (&x)[MGeo<HD>::NL],
   wave_lds_fence();
 }
 
+// Several query rows per workgroup: the V rows of this tile from mask_from on
+// are live for some columns only (the later query rows). The shared product
+// O += Vᵀ·P would give every other column 0·v for them: exactly 0 for a
+// finite v, but NaN where v is inf or NaN, while the causal mask leaves such a
+// row out of an earlier query row entirely. So in a tile that holds such rows
+// (rows j0 .. j1 - 1 of the tile, from mask_from to the workgroup's end row)
+// they are kept out of the product: stash_masked_rows copies them into the
+// wave's K area (free once the scores are computed; rows of 2*HD bytes) and
+// zeroes them in the staged V, and after the product add_masked_rows adds p·v
+// on the vector ALU for each lane's own column where the row is live
+// (tb + j < lim). Only the tiles that hold a block's newest rows take this
+// path. (Measured alternatives: the vector-ALU step between staging and
+// product raised the several-row kernels' registers by ~30; a check for
+// non-finite values that skips the path when there are none, and writing the
+// zeros and the copy while staging, both cost more than the path itself.)
+struct MaskedRows {
+  uint32_t j0, j1;
+};
+
+__device__ __forceinline__ MaskedRows masked_rows(uint32_t tb, uint32_t mask_from,
+                                                  uint32_t row_end) {
+  MaskedRows m;
+  m.j0 = mask_from > tb ? mask_from - tb : 0u;
+  m.j1 = row_end - tb < (uint32_t)kTileRows ? row_end - tb : (uint32_t)kTileRows;
+  return m;
+}
+
+template <int HD>
+__device__ __forceinline__ void stash_masked_rows(unsigned char *vlds,
+                                                  unsigned char *klds,
+                                                  MaskedRows m, int lane) {
+  using Geo = MGeo<HD>;
+  constexpr int CPR = HD / 8;  // 16-byte chunks per row
+  const int n = (int)(m.j1 - m.j0) * CPR;
+  for (int c = lane; c < n; c += 64) {
+    const uint32_t j = m.j0 + (uint32_t)(c / CPR);
+    uint4 *src = reinterpret_cast<uint4 *>(vlds + j * Geo::VSTR + (c % CPR) * 16);
+    *reinterpret_cast<uint4 *>(klds + (j - m.j0) * (2 * HD) + (c % CPR) * 16) = *src;
+    *src = uint4{0u, 0u, 0u, 0u};
+  }
+}
+
+// Lane (grp, col) holds dims 16b + 4grp + 0..3 of column col (the layout of
+// the product's accumulators); p of row j and column col sits in lane
+// 16 (j / 4) + col, entry j % 4. With one column block the lo-part lanes
+// (col >= 8) hold the same column as lane col - 8, so only the hi-part lanes
+// add; with two blocks every lane adds into the hi-part block.
+template <int HD, int CB>
+__device__ __forceinline__ void add_masked_rows(
+    const unsigned char *klds, MaskedRows m, uint32_t tb, uint32_t lim,
+    const float (&pv)[4], float4v (&oacc)[CB][MGeo<HD>::DB], int col, int grp,
+    bool hi_col) {
+  using Geo = MGeo<HD>;
+  const bool adds = (CB == 2) || hi_col;
+  for (uint32_t j = m.j0; j < m.j1; ++j) {
+    const uint32_t k = j % 4;
+    const float pk = k == 0 ? pv[0] : k == 1 ? pv[1] : k == 2 ? pv[2] : pv[3];
+    const float p = __shfl(pk, (int)(16 * (j / 4)) + col);
+    if (adds && tb + j < lim) {
+#pragma unroll
+      for (int b = 0; b < Geo::DB; ++b) {
+        const half4 v4 = *reinterpret_cast<const half4 *>(
+            klds + (j - m.j0) * (2 * HD) + (16 * b + 4 * grp) * 2);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          oacc[0][b][i] = __builtin_fmaf(p, (float)v4[i], oacc[0][b][i]);
+      }
+    }
+  }
+}
+
 // a4 + a5 for the loaded tile starting at row tb. mask_from: wave-uniform row
-// from which some column may be masked; lim: this lane's column's end row
-// (equal to mask_from with one query row per workgroup). SAFE: a column may
+// from which some column may be masked; row_end: the workgroup's end row (no
+// column sees a row past it); lim: this lane's column's end row (equal to
+// mask_from with one query row per workgroup). SAFE: a column may
 // have no live row yet (several query rows per workgroup), so -inf maxima are
 // guarded. K is staged first and V only after the softmax, so the V rows
 // (which arrive last) are written while the exponentials run.
@@ -296,7 +368,8 @@ template <int HD, bool SAFE, int CB, typename AfterK, typename AfterV>
 __device__ __forceinline__ void compute_tile(
     TileRegs<HD> &t, AfterK after_k, AfterV after_v, unsigned char *slice,
     uint32_t tb,
-    uint32_t mask_from, uint32_t lim, const half8 (&qf)[CB][MGeo<HD>::KS],
+    uint32_t mask_from, uint32_t row_end, uint32_t lim,
+    const half8 (&qf)[CB][MGeo<HD>::KS],
     float4v (&oacc)[CB][MGeo<HD>::DB], float &m_run, float &m_true,
     float &s_run, int col, int grp, int lane, bool hi_col) {
   using Geo = MGeo<HD>;
@@ -392,6 +465,10 @@ __device__ __forceinline__ void compute_tile(
   // the same row order as its p values.
   stage_rows<HD, Geo::VSTR>(t.v, vlds, lane);
   after_v(t);
+  const MaskedRows mr = masked_rows(tb, mask_from, row_end);
+  const bool split_rows =
+      SAFE && tb + kTileRows > mask_from && mask_from < row_end;
+  if (split_rows) stash_masked_rows<HD>(vlds, slice, mr, lane);
   const int c4 = col >> 2;
   const int cm = col & 3;
 #pragma unroll
@@ -405,6 +482,8 @@ __device__ __forceinline__ void compute_tile(
       oacc[cb][b] = __builtin_amdgcn_mfma_f32_16x16x16f16(
           __builtin_bit_cast(half4, r0), pf[cb], oacc[cb][b], 0, 0, 0);
   }
+  if (split_rows)
+    add_masked_rows<HD, CB>(slice, mr, tb, lim, pv, oacc, col, grp, hi_col);
   __builtin_amdgcn_s_setprio(0);
 }
 
@@ -707,8 +786,8 @@ partial_mfma_kernel(PartialArgs a) {
           [&](TileRegs<HD> &x) {
             if (kEarly && more) load_rows<HD>(x.v, vseq, row_bytes, nt, hi32, off);
           },
-          slice, t0, mask32, lim32, qf, oacc, m_run, m_true, s_run, col, grp,
-          lane, hi_col);
+          slice, t0, mask32, hi32, lim32, qf, oacc, m_run, m_true, s_run, col,
+          grp, lane, hi_col);
       t0 = nt;
       if (!more) break;
       if constexpr (!kEarly) load_tile<HD>(tr, kseq, vseq, row_bytes, t0, hi32, off);

@@ -183,12 +183,15 @@ int splitkv_partial(const float *q, const uint16_t *k_cache,
  * batch * n_q > 65535 or n_q * n_head > 65535. n_q = 1 is exactly
  * splitkv_partial / splitkv_decode_attn. The combine of these records is
  * splitkv_combine with n_head -> n_q * n_head.
- * Restriction: rows that share a workgroup multiply every staged V row into
- * every row's output with a weight of exactly 0 where the row is not yet
- * visible, so a non-finite V value in one of the n_q - 1 newest cache rows
- * (e.g. an fp16 overflow in the appended values) turns the outputs of the
- * earlier query rows of that block into NaN, where the definition leaves
- * them finite. Finite caches are unaffected. */
+ * Non-finite cache values: a cache row that a query row cannot see yet does
+ * not reach that row's output, whatever it holds (rows that share a
+ * workgroup take the newest rows, which only some of them see, through a
+ * separate per-column step). A V row that a query row does see and that
+ * holds inf or NaN (e.g. an fp16 overflow in appended values) makes that
+ * row's output non-finite in the same places as the definition, possibly NaN
+ * where the definition gives +-inf: the weight p enters the matrix product
+ * as two fp16 parts, and inf times the low part can be 0 * inf or have the
+ * opposite sign. */
 int splitkv_partial_rows(const float *q, const uint16_t *k_cache,
                          const uint16_t *v_cache, const int32_t *positions,
                          float *partials, int batch, int n_q, int n_head,

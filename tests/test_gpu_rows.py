@@ -103,6 +103,45 @@ def test_rows_full_length(n_q):
                 np.array_equal(lohi[:, 1], hi)
 
 
+
+@pytest.mark.parametrize("hd", [64, 128, 256])
+def test_rows_nonfinite_v_only_later_rows_see(hd):
+    """The newest cache rows are seen by the later query rows of a block
+    only (the causal mask of #199 comment 1 section 2). With inf, -inf and
+    NaN in such V rows, the earlier query rows must be exactly as if those
+    rows were absent: finite and within the bar. The rows that see them must
+    be non-finite exactly where the oracle is and within the bar elsewhere
+    (an inf reaches the product through the two fp16 parts of p, whose sum
+    can be NaN where the definition gives +-inf, so only finiteness is
+    compared). Row blocks of one and two MFMA column blocks, and the paired
+    grid (16 splits)."""
+    T = 300
+    cases = [(1, 2, 8), (2, 2, 4), (4, 1, 2), (3, 1, 4), (7, 1, 2)]
+    for G, nkvh, n_q in cases:
+        nh = G * nkvh
+        pos = [T - 1, 150, n_q + 20, 64]
+        q, k, v, p = _rows_case(700 + hd + G, 4, n_q, nh, nkvh, hd, T, pos)
+        # query row t sits at pos - (n_q - 1 - t): cache row pos - j is seen
+        # by the query rows t >= n_q - 1 - j only
+        poison = [(0, np.inf), (1, np.nan), (2, -np.inf)]
+        for b in range(4):
+            for j, val in poison:
+                if j < n_q - 1:
+                    v[b, pos[b] - j, b % nkvh, (7 * j + b) % hd] = val
+        scale = float(np.float32(1 / np.sqrt(hd)))
+        want = oracle.decode_attn_rows(q, k, v, p, nkvh, scale)
+        assert not np.isfinite(want).all()
+        for S in (1, 7, 16):
+            what = f"rows non-finite V hd={hd} G={G} n_q={n_q} S={S}"
+            say(what)
+            got, _ = _run_rows(q, k, v, p, S, 0, scale)
+            fin = np.isfinite(want)
+            assert np.array_equal(np.isfinite(got), fin), what
+            parity(got[fin], want[fin], what, "rows, non-finite V in the newest rows")
+            # the first query row of every sequence sees none of them
+            assert np.isfinite(got[:, 0]).all(), what
+
+
 def test_one_row_equals_decode():
     """n_q = 1 through the rows entry point is the one-row decode, bit for
     bit, records included."""
