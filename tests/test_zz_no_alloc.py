@@ -60,3 +60,48 @@ def test_noalloc_rejects_oversize_records():
     assert e.value.status == -5
     torch.cuda.synchronize()
     assert torch.count_nonzero(out).item() == 0
+
+
+def test_noalloc_in_a_graph_matches_decode_attn():
+    """The use this entry point is for: captured in a hipGraph (after one
+    call outside capture on the device), then replayed as the context grows.
+    Every replay's output is bit-identical to splitkv_decode_attn on the same
+    inputs, with eager calls of both entry points between the replays."""
+    import decode_attention_gqa_amd as skv
+    torch = torch_mod()
+    sh = synth.Shape(1, 28, 4, 128, 4096)
+    case = synth.make_case(3, sh, 4096)
+    q, k, v, _ = to_device(case)
+    pos = torch.zeros(1, dtype=torch.int32, device="cuda")
+    S, blk = skv.pick_splits(1, 28, 4, 128, 4096, 256)
+    out = torch.full((1, 28, 128), float("nan"), device="cuda")
+    part, out_ref = alloc_outputs(sh, S)
+
+    def step():
+        skv.decode_attn_noalloc(q, k, v, pos, out, S, blk, case.scale)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()                                   # first call outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    say(f"noalloc graph capture S={S}")
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    for nkv in (1, 17, 1000, 4096, 300):
+        pos.fill_(nkv - 1)
+        say(f"noalloc graph replay nkv={nkv}")
+        out.fill_(float("nan"))
+        graph.replay()
+        torch.cuda.synchronize()
+        got = out.cpu().numpy().copy()
+        skv.decode_attn(q, k, v, pos, part, out_ref, S, blk, case.scale)
+        step()                                   # eager noalloc between replays
+        torch.cuda.synchronize()
+        want = out_ref.cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), nkv
+        assert np.array_equal(out.cpu().numpy().view(np.uint32),
+                              want.view(np.uint32)), nkv
