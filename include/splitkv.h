@@ -173,12 +173,12 @@ int splitkv_partial(const float *q, const uint16_t *k_cache,
  * The splits are cut from the last row's live length positions[b] + 1, as
  * for one row; row t's rows end at min(hi, its live length). One partial
  * workgroup per (split, KV head, sequence, block of rows): a block holds the
- * rows whose (row, head) pairs fit the workgroup's MFMA columns (G * R <= 8
- * in one 16-column block, or two rows at G = 5..8 in two blocks for
- * head_dim 64 and 128; one row otherwise and for head_dim 8/16/32), one
- * workgroup per (split, KV head, sequence, block of R rows); each K/V row is
- * read once per block, and when n_splits is a multiple of 8 the blocks of
- * one split run side by side so that the later reads hit the cache. Other arguments and errors as for
+ * R rows whose (row, head) pairs fit the workgroup's MFMA columns (G * R <= 8
+ * in one 16-column block; at head_dim 64 and 128 up to 16 pairs in two
+ * blocks: two rows at G = 5..8, four at G = 3 and 4, eight at G = 2; one row
+ * otherwise and at head_dim 8/16/32). Each K/V row is read once per block,
+ * and when n_splits is a multiple of 8 the blocks of one split run side by
+ * side so that the later reads hit the cache. Other arguments and errors as for
  * splitkv_partial / splitkv_decode_attn, plus SPLITKV_EINVAL when n_q < 1,
  * batch * n_q > 65535 or n_q * n_head > 65535. n_q = 1 is exactly
  * splitkv_partial / splitkv_decode_attn. The combine of these records is
