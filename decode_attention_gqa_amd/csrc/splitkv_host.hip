@@ -248,6 +248,17 @@ int splitkv_pick_splits_rows(int batch, int n_q, int n_head, int n_kv_head,
   // has the same work, so a single round is best; a few workgroups past it
   // would cost a whole second round, hence the floor.
   long long s = wpc * cu_count / units;
+  // With 8-wave workgroups (head_dim 256) a split of up to 8 tiles (128
+  // rows) is computed in one round of its waves; more splits than the
+  // full-length rows need for that add records (a longer combine) and
+  // per-split fixed costs, not parallelism the memory system can use
+  // (16q/2kv, max_ctx 8,400: 66 splits 10.77 against 11.08 us per layer at
+  // 128 at the full length, 8.12 against 8.70 at 1,024 rows, within 0.1 us
+  // at 2,048-6,000).
+  if (head_dim >= 256) {
+    const long long fit = ((long long)max_ctx + 127) / 128;
+    if (s > fit) s = fit;
+  }
   // With several sequences the lengths can differ and the host does not see
   // them: about 16 workgroups per compute unit let the dispatcher balance
   // the load, as long as a full-length split still has ~1024 rows to

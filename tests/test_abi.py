@@ -67,10 +67,13 @@ def test_pick_splits_properties(lib):
     # Values the rule gives on 256 compute units. One sequence: one full round
     # of resident workgroups (2 per compute unit at hd128 -> 128 splits over 4
     # KV heads; 1 at hd256 -> 128 over 2), capped so a full-length split
-    # keeps one 32-row tile (2048 / 32 -> 64; 256 / 32 -> 8). Batches: ~16
-    # workgroups per compute unit, splits of >= 1024 rows.
+    # keeps one 32-row tile (2048 / 32 -> 64; 256 / 32 -> 8), and at hd256
+    # (8 waves) at the splits whose full length fills one 16-row tile per
+    # wave (ceil(8400 / 128) -> 66). Batches: ~16 workgroups per compute
+    # unit, splits of >= 1024 rows.
     cases = {(1, 28, 4, 128, 33024): 128, (1, 28, 4, 128, 2048): 64,
-             (1, 16, 2, 256, 8400): 128, (32, 32, 8, 128, 32768): 16,
+             (1, 16, 2, 256, 8400): 66, (1, 16, 2, 256, 33024): 128,
+             (32, 32, 8, 128, 32768): 16,
              (16, 32, 8, 128, 32768): 32, (8, 32, 8, 128, 32768): 32,
              (4, 32, 8, 128, 32768): 32, (32, 32, 8, 128, 4096): 4,
              (1, 4, 2, 64, 256): 8, (1, 28, 4, 128, 40): 1,
