@@ -253,8 +253,8 @@ int splitkv_pick_splits_rows(int batch, int n_q, int n_head, int n_kv_head,
   // full-length rows need for that add records (a longer combine) and
   // per-split fixed costs, not parallelism the memory system can use
   // (16q/2kv, max_ctx 8,400: 66 splits 10.77 against 11.08 us per layer at
-  // 128 at the full length, 8.12 against 8.70 at 1,024 rows, within 0.1 us
-  // at 2,048-6,000).
+  // 128 at the full length, 8.12 against 8.70 at 1,024 rows; 0.05-0.12 us
+  // slower at 2,048-4,096 rows, 0.05 faster at 6,000).
   if (head_dim >= 256) {
     const long long fit = ((long long)max_ctx + 127) / 128;
     if (s > fit) s = fit;
