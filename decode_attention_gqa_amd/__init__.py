@@ -35,7 +35,7 @@ LIB_PATH = os.environ.get("SPLITKV_LIB") or os.path.join(
     os.path.dirname(os.path.abspath(__file__)), "libsplitkv.so")
 SUPPORTED_HEAD_DIMS = (8, 16, 32, 64, 128, 256)
 MAX_GROUP = 8
-ABI_VERSION = 2
+ABI_VERSION = 3
 NOALLOC_SCRATCH_BYTES = 16 << 20   # SPLITKV_NOALLOC_SCRATCH_BYTES
 
 _lock = threading.Lock()
@@ -248,7 +248,7 @@ def _rows_shapes(q, k_cache, v_cache, positions):
 def partial_rows(q, k_cache, v_cache, positions, partials, n_splits: int,
                  block_len: int = 0, scale: float | None = None, stream=None):
     """Partial kernel for several query rows per sequence (q [B][n_q][nh][hd],
-    causal within the rows; records [B][S][n_q*nh][4+hd])."""
+    causal within the rows; the records of ``partial`` with n_q*nh heads)."""
     B, n_q, nh, nkvh, hd, max_ctx = _rows_shapes(q, k_cache, v_cache, positions)
     _partials_ok(partials, B, n_q * nh, hd, n_splits)
     scale = 1.0 / math.sqrt(hd) if scale is None else float(scale)

@@ -7,6 +7,11 @@
 // A record with mx = -inf (an idle split) gets weight exactly 0, also when all
 // records are idle and gmx itself is -inf.
 //
+// The records' output sums are [batch][n_splits][n_head][head_dim] and their
+// headers {mx, S, lo, hi} [batch][n_head][n_splits][4], so a 32-dim slice of
+// a record is one aligned 128-byte line and a head's headers are contiguous:
+// each line is fetched by one workgroup only.
+//
 // Grid dim3(n_head, head_dim / DC, batch): one workgroup per (query head,
 // slice of DC head dims, sequence), so the merge reads are spread over many
 // compute units. Inside, C = DC/4 threads cover one record's slice with
@@ -100,7 +105,6 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   constexpr int DC = Geo::DC;
   constexpr int C = Geo::C;
   constexpr int NG = Geo::NG;
-  constexpr size_t pstr = 4 + HD;
 
   const int h = blockIdx.x;
   const int d_base = blockIdx.y * DC;
@@ -108,17 +112,22 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
   const int tid = threadIdx.x;
   const int c = tid % C;
   const int g0 = tid / C;
-  const size_t rstride = (size_t)a.n_head * pstr;
-  const float *base =
-      a.partials + ((size_t)b * a.n_splits * a.n_head + h) * pstr;
-  const int dofs = 4 + d_base + 4 * c;
-  // The records of this (sequence, head) through one raw buffer view based
-  // at its first record: the per-record offsets are 32-bit (the host keeps a
-  // sequence's records below 2 GiB), with no 64-bit address arithmetic per
-  // load (28q hd128 at 32K rows, 128 splits: 3.21 against 3.28-3.33 us).
+  // The output sums of this (sequence, head), one record every n_head * HD
+  // floats, and its headers, 4 floats apart, each through one raw buffer
+  // view based at the first record: the per-record offsets are 32-bit (the
+  // host keeps a sequence's records below 2 GiB), with no 64-bit address
+  // arithmetic per load (28q hd128 at 32K rows, 128 splits: 3.21 against
+  // 3.28-3.33 us).
+  const float *obase =
+      a.partials + ((size_t)b * a.n_splits * a.n_head + h) * HD;
+  const float *hbase =
+      a.headers + ((size_t)b * a.n_head + h) * a.n_splits * 4;
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float *>(base), (short)0, 0x7FFFFFFF, 0x00020000);
-  const uint32_t rbytes = (uint32_t)(rstride * sizeof(float));
+      const_cast<float *>(obase), (short)0, 0x7FFFFFFF, 0x00020000);
+  const __amdgpu_buffer_rsrc_t hb = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float *>(hbase), (short)0, 0x7FFFFFFF, 0x00020000);
+  const uint32_t rbytes = (uint32_t)((size_t)a.n_head * HD * sizeof(float));
+  const uint32_t dofs = (uint32_t)(d_base + 4 * c) * 4u;
 
   float m = neg_inf(), s = 0.0f;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -131,10 +140,10 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(CombineArgs a) {
       hdr[u] = make_float2(neg_inf(), 0.0f);
       oc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (sp < a.n_splits) {
-        const uint32_t ro = (uint32_t)sp * rbytes;
-        const auto h2 = __builtin_amdgcn_raw_buffer_load_b64(rb, (int)ro, 0, 0);
+        const auto h2 = __builtin_amdgcn_raw_buffer_load_b64(
+            hb, (int)(16u * (uint32_t)sp), 0, 0);
         const auto o4 = __builtin_amdgcn_raw_buffer_load_b128(
-            rb, (int)(ro + 4u * (uint32_t)dofs), 0, 0);
+            rb, (int)((uint32_t)sp * rbytes + dofs), 0, 0);
         hdr[u] = make_float2(__builtin_bit_cast(float, (unsigned)h2[0]),
                              __builtin_bit_cast(float, (unsigned)h2[1]));
         oc[u] = make_float4(__builtin_bit_cast(float, (unsigned)o4[0]),

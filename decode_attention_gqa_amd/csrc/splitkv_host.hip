@@ -93,6 +93,16 @@ int check_combine(const float *partials, const float *out, int batch,
   return SPLITKV_OK;
 }
 
+// The records buffer holds the output sums of every record first
+// ([batch][n_splits][rec_heads][head_dim]), then their 4-float headers
+// ([batch][rec_heads][n_splits][4]); rec_heads = n_q * n_head.
+template <typename T>
+T *headers_of(T *partials, int batch, int rec_heads, int head_dim,
+              int n_splits) {
+  return partials +
+         (size_t)batch * n_splits * rec_heads * (size_t)head_dim;
+}
+
 int do_partial(const float *q, const uint16_t *k, const uint16_t *v,
                const int32_t *positions, float *partials, int batch,
                int n_head, int n_kv_head, int head_dim, int max_ctx,
@@ -106,6 +116,7 @@ int do_partial(const float *q, const uint16_t *k, const uint16_t *v,
   a.v = v;
   a.positions = positions;
   a.partials = partials;
+  a.headers = headers_of(partials, batch, n_q * n_head, head_dim, n_splits);
   a.n_head = n_head;
   a.n_kv_head = n_kv_head;
   a.max_ctx = max_ctx;
@@ -159,6 +170,7 @@ int do_combine(const float *partials, float *out, int batch, int n_head,
                int head_dim, int n_splits, void *stream) {
   splitkv::CombineArgs a;
   a.partials = partials;
+  a.headers = headers_of(partials, batch, n_head, head_dim, n_splits);
   a.out = out;
   a.n_head = n_head;
   a.n_splits = n_splits;

@@ -14,7 +14,9 @@ struct PartialArgs {
   const uint16_t *k;         // [B][max_ctx][n_kv_head][HD] fp16 bits
   const uint16_t *v;         // same layout
   const int32_t *positions;  // [B]
-  float *partials;           // [B][n_splits][n_q * n_head][4 + HD]
+  // Split records of record head H = t * n_head + h (t the query row):
+  float *partials;           // oc sums [B][n_splits][n_q * n_head][HD]
+  float *headers;            // {mx, S, lo, hi} [B][n_q * n_head][n_splits][4]
   int n_head;
   int n_kv_head;
   int max_ctx;
@@ -41,7 +43,8 @@ struct PartialArgs {
 };
 
 struct CombineArgs {
-  const float *partials;
+  const float *partials;     // oc sums [B][n_splits][n_head][HD]
+  const float *headers;      // {mx, S, lo, hi} [B][n_head][n_splits][4]
   float *out;                // [B][n_head][HD]
   int n_head;
   int n_splits;

@@ -104,17 +104,23 @@ __device__ __forceinline__ long long row_end(const PartialArgs &a,
   return row_end_at(a, rs.b, rs.t, hi);
 }
 
-// Offsets of query row t of sequence b: its first q element and its first
-// record ([B][S][n_q * n_head][4 + HD], record head index t * n_head + h).
+// Offsets for query row t of sequence b: its first q element, and the parts
+// of the record of split sp and record head t * n_head + head: the first of
+// its HD output sums ([B][S][n_q * n_head][HD]) and its 4-float header
+// ([B][n_q * n_head][S][4]).
 __device__ __forceinline__ size_t q_offset(const PartialArgs &a,
                                            const RowSel &rs, int head, int hd) {
   return (((size_t)rs.b * a.n_q + rs.t) * a.n_head + head) * (size_t)hd;
 }
-__device__ __forceinline__ size_t rec_offset(const PartialArgs &a,
-                                             const RowSel &rs, int sp,
-                                             int head, int hd) {
+__device__ __forceinline__ size_t oc_offset(const PartialArgs &a,
+                                            const RowSel &rs, int sp,
+                                            int head, int hd) {
   return ((((size_t)rs.b * a.n_splits + sp) * a.n_q + rs.t) * a.n_head +
-          head) * (size_t)(4 + hd);
+          head) * (size_t)hd;
+}
+__device__ __forceinline__ size_t hdr_offset(const PartialArgs &a, int b,
+                                             int t, int sp, int head) {
+  return ((((size_t)b * a.n_q + t) * a.n_head + head) * a.n_splits + sp) * 4;
 }
 
 // Merge (m2, s2) into (m, s) and return the weights (c1, c2) applied to the
@@ -136,16 +142,15 @@ __device__ __forceinline__ MergeW merge_weights(float &m, float &s, float m2,
 
 // Final step of a partial workgroup: the kWaves per-wave states in LDS
 // (max and sum per head in base-2 units, unnormalised output per head and
-// dim) are merged exactly and written as records
-// { mx (natural-log units), S, lo, hi, oc[0..HD) } for the G query heads of
-// KV head hk. Must be called by all threads after a barrier.
+// dim) are merged exactly and written as the records of the G query heads of
+// KV head hk: oc[0..HD) and the header { mx (natural-log units), S, lo, hi }.
+// Must be called by all threads after a barrier.
 template <int HD, int G>
 __device__ __forceinline__ void write_records(
     const PartialArgs &a, int sp, int hk, const RowSel &rs,
     const SplitRange &rg, const float (&sm_m)[kWaves][G],
     const float (&sm_s)[kWaves][G], const float (&sm_o)[kWaves][G][HD]) {
-  const size_t pstr = 4 + HD;
-  float *rec0 = a.partials + rec_offset(a, rs, sp, hk * G, HD);
+  float *oc0 = a.partials + oc_offset(a, rs, sp, hk * G, HD);
   for (int idx = threadIdx.x; idx < G * HD; idx += kThreads) {
     const int g = idx / HD;
     const int d = idx % HD;
@@ -160,14 +165,13 @@ __device__ __forceinline__ void write_records(
       s = fmaf(c, sm_s[w][g], s);
       o = fmaf(c, sm_o[w][g][d], o);
     }
-    float *rec = rec0 + (size_t)g * pstr;
-    rec[4 + d] = o;
-    if (d == 0) {
-      rec[0] = m * kLn2;  // -inf stays -inf
-      rec[1] = s;
-      rec[2] = __builtin_bit_cast(float, (int32_t)rg.lo);
-      rec[3] = __builtin_bit_cast(float, (int32_t)rg.hi);
-    }
+    oc0[(size_t)g * HD + d] = o;
+    if (d == 0)
+      *reinterpret_cast<float4 *>(a.headers +
+                                  hdr_offset(a, rs.b, rs.t, sp, hk * G + g)) =
+          make_float4(m * kLn2,  // -inf stays -inf
+                      s, __builtin_bit_cast(float, (int32_t)rg.lo),
+                      __builtin_bit_cast(float, (int32_t)rg.hi));
   }
 }
 

@@ -812,8 +812,9 @@ partial_mfma_kernel(PartialArgs a) {
   // before any of the arithmetic.
   s_run = pair32_sum(pair16_sum(s_run));
   constexpr int D4 = HD / 4;
-  const size_t pstr = 4 + HD;
-  float *rec0 = a.partials + detail::rec_offset(a, rs, sp, hy * G, HD);
+  // Output sums of column (row r, head g): oc0 + (r * n_head + g) * HD; its
+  // header at hdr_offset(rs.b, rs.t + r, sp, hy * G + g).
+  float *oc0 = a.partials + detail::oc_offset(a, rs, sp, hy * G, HD);
 
   // A split of at most one tile (short contexts over many splits), or an
   // idle one: only wave 0 can have rows, so it writes the records straight
@@ -834,8 +835,8 @@ partial_mfma_kernel(PartialArgs a) {
     const int r = col / G;
     if (R > 1 && rs.t + r >= a.n_q) return;
     const float c = (m_run == neg_inf()) ? 0.0f : fast_exp2(m_run - m_true);
-    float *rec = rec0 + (size_t)(col - r * G) * pstr +
-                 (size_t)r * a.n_head * pstr;
+    const int g = col - r * G;
+    float *oc = oc0 + (size_t)(r * a.n_head + g) * HD;
 #pragma unroll
     for (int i = 0; i < Geo::DB; ++i) {
       float4 o;
@@ -843,13 +844,14 @@ partial_mfma_kernel(PartialArgs a) {
       o.y = fmaf(c, osum[i][1], 0.0f) + 0.0f;
       o.z = fmaf(c, osum[i][2], 0.0f) + 0.0f;
       o.w = fmaf(c, osum[i][3], 0.0f) + 0.0f;
-      *reinterpret_cast<float4 *>(rec + 4 + 16 * i + 4 * grp) = o;
+      *reinterpret_cast<float4 *>(oc + 16 * i + 4 * grp) = o;
     }
     if (grp == 0)
-      *reinterpret_cast<float4 *>(rec) = make_float4(
-          m_true * detail::kLn2, fmaf(c, s_run, 0.0f) + 0.0f,
-          __builtin_bit_cast(float, (int32_t)rg.lo),
-          __builtin_bit_cast(float, (int32_t)rg.hi));
+      *reinterpret_cast<float4 *>(
+          a.headers + detail::hdr_offset(a, rs.b, rs.t + r, sp, hy * G + g)) =
+          make_float4(m_true * detail::kLn2, fmaf(c, s_run, 0.0f) + 0.0f,
+                      __builtin_bit_cast(float, (int32_t)rg.lo),
+                      __builtin_bit_cast(float, (int32_t)rg.hi));
     return;
   }
 
@@ -893,13 +895,15 @@ partial_mfma_kernel(PartialArgs a) {
       acc.w = fmaf(c, x[w].w, acc.w);
       st = fmaf(c, stw[w].z, st);
     }
-    float *rec = rec0 + (size_t)(gg - r * G) * pstr +
-                 (size_t)r * a.n_head * pstr;  // row t + r: n_head records on
-    *reinterpret_cast<float4 *>(rec + 4 + 4 * d4) = acc;
+    const int g = gg - r * G;  // row t + r: n_head record heads on
+    *reinterpret_cast<float4 *>(oc0 + (size_t)(r * a.n_head + g) * HD +
+                                4 * d4) = acc;
     if (d4 == 0)
-      *reinterpret_cast<float4 *>(rec) = make_float4(
-          mm * detail::kLn2, st, __builtin_bit_cast(float, (int32_t)rg.lo),
-          __builtin_bit_cast(float, (int32_t)rg.hi));
+      *reinterpret_cast<float4 *>(
+          a.headers + detail::hdr_offset(a, rs.b, rs.t + r, sp, hy * G + g)) =
+          make_float4(mm * detail::kLn2, st,
+                      __builtin_bit_cast(float, (int32_t)rg.lo),
+                      __builtin_bit_cast(float, (int32_t)rg.hi));
   }
 }
 

@@ -40,13 +40,21 @@
  *              stride_kv = n_kv_head*head_dim); fp16 values are passed as their
  *              IEEE binary16 bit patterns (uint16_t).
  *   positions int32    [batch]                               4-byte aligned
- *   partials  float32  [batch][n_splits][n_head][4 + head_dim] 16-byte aligned
- *             record = { mx, S, lo, hi, oc[0..head_dim) }: mx is the largest
- *             score of the split (natural-log units, -inf when the split is
- *             idle), S the sum of exp(score - mx), oc the exp-weighted V sum
- *             (not normalised), lo/hi the split's row range as int32 bit
- *             patterns ("10 · R4", sections 2.1 and 3.2; slots 2 and 3 are
- *             unused padding on the page).
+ *   partials  float32, splitkv_partials_bytes(...) bytes, 16-byte aligned:
+ *             one record per (sequence, split, query head) = { mx, S, lo, hi,
+ *             oc[0..head_dim) }: mx is the largest score of the split
+ *             (natural-log units, -inf when the split is idle), S the sum of
+ *             exp(score - mx), oc the exp-weighted V sum (not normalised),
+ *             lo/hi the split's row range as int32 bit patterns ("10 · R4",
+ *             sections 2.1 and 3.2; slots 2 and 3 are unused padding on the
+ *             page). The buffer holds every record's oc first, then every
+ *             record's 4-float header { mx, S, lo, hi }:
+ *               oc      at float [((b*n_splits + sp)*n_head + h)*head_dim]
+ *               header  at float batch*n_splits*n_head*head_dim
+ *                                + ((b*n_head + h)*n_splits + sp)*4
+ *             (the page stores each record's fields together; apart, a
+ *             32-dim slice of oc is one aligned 128-byte line and a head's
+ *             headers are contiguous for the combine).
  *   out       float32  [batch][n_head][head_dim]             16-byte aligned
  *
  * Split rule ("10 · R4", section 2.2; "Red Lite dev35", Change): with
@@ -92,7 +100,7 @@ extern "C" {
 #define SPLITKV_ELAUNCH (-4)      /* the HIP runtime refused a launch         */
 #define SPLITKV_ESCRATCH (-5)     /* records exceed the no-alloc scratch      */
 
-#define SPLITKV_ABI_VERSION 2
+#define SPLITKV_ABI_VERSION 3
 
 /* Capacity of the device-resident scratch of splitkv_decode_attn_noalloc. */
 #define SPLITKV_NOALLOC_SCRATCH_BYTES (16u << 20)
@@ -166,9 +174,9 @@ int splitkv_partial(const float *q, const uint16_t *k_cache,
  * (splitkv_append_kv with n_rows = n_q does that).
  *   q         device fp32 [batch][n_q][n_head][head_dim], 16-byte aligned.
  *   partials  splitkv_partials_bytes(batch, n_q * n_head, head_dim,
- *             n_splits) bytes; records [batch][n_splits][n_q * n_head]
- *             [4 + head_dim], record head index t * n_head + h, slots [2],
- *             [3] the split's bounds (those of the last row's live length).
+ *             n_splits) bytes; the records of splitkv_partial with n_head
+ *             -> n_q * n_head (record head index t * n_head + h), lo and hi
+ *             the split's bounds (those of the last row's live length).
  *   out       device fp32 [batch][n_q][n_head][head_dim].
  * The splits are cut from the last row's live length positions[b] + 1, as
  * for one row; row t's rows end at min(hi, its live length). One partial

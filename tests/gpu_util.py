@@ -19,6 +19,25 @@ REL_TOL = 1e-3
 WORST: dict = {}
 
 
+def records_view(buf, B, S, NH, hd):
+    """The library's records buffer (flat float32: the output sums of every
+    record [B][S][NH][hd], then the headers {mx, S, lo, hi} [B][NH][S][4]) as
+    one array [B][S][NH][4 + hd] of records {mx, S, lo, hi, oc[0..hd)}, the
+    layout the oracle uses."""
+    buf = np.asarray(buf).reshape(-1)
+    n_oc = B * S * NH * hd
+    oc = buf[:n_oc].reshape(B, S, NH, hd)
+    hdr = buf[n_oc:n_oc + B * NH * S * 4].reshape(B, NH, S, 4)
+    return np.concatenate([hdr.transpose(0, 2, 1, 3), oc], axis=-1)
+
+
+def pack_records(rec):
+    """Inverse of records_view: records [B][S][NH][4 + hd] to the flat buffer."""
+    rec = np.asarray(rec)
+    return np.concatenate([rec[..., 4:].reshape(-1),
+                           rec[..., :4].transpose(0, 2, 1, 3).reshape(-1)])
+
+
 def say(*parts):
     """Name the case about to run on the GPU, flushed, so a crash log shows it."""
     print("[gpu-case]", *parts, flush=True)
@@ -64,8 +83,8 @@ def run_gpu(case, n_splits, block_len=0, dev=None):
     part, out = alloc_outputs(sh, n_splits)
     skv.decode_attn(q, k, v, pos, part, out, n_splits, block_len, case.scale)
     torch.cuda.synchronize()
-    rec = part.cpu().numpy().reshape(sh.batch, n_splits, sh.n_head,
-                                     4 + sh.head_dim)
+    rec = records_view(part.cpu().numpy(), sh.batch, n_splits, sh.n_head,
+                       sh.head_dim)
     return out.cpu().numpy(), rec
 
 

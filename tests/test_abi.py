@@ -38,7 +38,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_strerror(lib):
-    assert lib.splitkv_abi_version() == 2
+    assert lib.splitkv_abi_version() == 3
     texts = {c: skv.strerror(c)
              for c in (OK, EINVAL, EUNSUP, EALIGN, ELAUNCH, ESCRATCH)}
     assert len(set(texts.values())) == 6

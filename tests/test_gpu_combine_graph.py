@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import parity, say, to_device, torch_mod
+from gpu_util import pack_records, parity, say, to_device, torch_mod
 
 pytestmark = pytest.mark.gpu
 
@@ -36,7 +36,7 @@ def test_combine_alone(hd):
         B, nh = 2, 6
         rec = _combine_case(hd * 1000 + S, B, S, nh, hd, idle).astype(np.float32)
         want = oracle.combine(rec.astype(np.float64))
-        part = torch.from_numpy(rec.reshape(-1)).cuda()
+        part = torch.from_numpy(pack_records(rec)).cuda()
         out = torch.full((B, nh, hd), float("nan"), device="cuda")
         say(f"combine hd={hd} S={S}")
         skv.combine(part, out, S)

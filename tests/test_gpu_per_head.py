@@ -11,7 +11,8 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import alloc_outputs, parity, say, to_device, torch_mod
+from gpu_util import (alloc_outputs, parity, records_view, say, to_device,
+                      torch_mod)
 
 pytestmark = pytest.mark.gpu
 
@@ -37,8 +38,8 @@ def test_per_head_equals_grouped(hd):
             skv.partial_per_head(q, k, v, pos, pb, S, blk, case.scale)
             skv.combine(pb, out, S)
             torch.cuda.synchronize()
-            ra = pa.cpu().numpy().reshape(sh.batch, S, sh.n_head, 4 + hd)
-            rb = pb.cpu().numpy().reshape(sh.batch, S, sh.n_head, 4 + hd)
+            ra = records_view(pa.cpu().numpy(), sh.batch, S, sh.n_head, hd)
+            rb = records_view(pb.cpu().numpy(), sh.batch, S, sh.n_head, hd)
             diff = ra.view(np.uint32) != rb.view(np.uint32)
             if diff.any():
                 idx = np.argwhere(diff)

@@ -8,7 +8,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import parity, say, torch_mod
+from gpu_util import parity, records_view, say, torch_mod
 
 pytestmark = pytest.mark.gpu
 
@@ -31,7 +31,7 @@ def _run_rows(q, k, v, pos, S, blk, scale):
     out = torch.full((B, n_q, nh, hd), float("nan"), device="cuda")
     skv.decode_attn_rows(d[0], d[1], d[2], d[3], part, out, S, blk, scale)
     torch.cuda.synchronize()
-    rec = part.cpu().numpy().reshape(B, S, n_q * nh, 4 + hd)
+    rec = records_view(part.cpu().numpy(), B, S, n_q * nh, hd)
     return out.cpu().numpy(), rec
 
 
