@@ -193,8 +193,8 @@ int splitkv_partial(const float *q, const uint16_t *k_cache,
  * splitkv_combine with n_head -> n_q * n_head.
  * Non-finite cache values: a cache row that a query row cannot see yet does
  * not reach that row's output, whatever it holds (rows that share a
- * workgroup take the newest rows, which only some of them see, through a
- * separate per-column step). A V row that a query row does see and that
+ * workgroup check the newest rows, which only some of them see, and take
+ * any that hold an inf or NaN through a separate per-column step). A V row that a query row does see and that
  * holds inf or NaN (e.g. an fp16 overflow in appended values) makes that
  * row's output non-finite in the same places as the definition, possibly NaN
  * where the definition gives +-inf: the weight p enters the matrix product
