@@ -92,6 +92,23 @@ def test_empty_and_single_row():
                       "edges nkv 0/1/clamped")
 
 
+@pytest.mark.parametrize("hd", [16, 128])
+def test_int32_extreme_positions(hd):
+    """positions at the int32 extremes: INT32_MAX is clamped to max_ctx
+    (no overflow of positions + 1), INT32_MIN is an empty context."""
+    shape = synth.Shape(3, 8, 2, hd, 64)
+    case = synth.make_case(9, shape, [64, 0, 6], poison_tail=True)
+    case.positions[:] = [2**31 - 1, -2**31, 5]
+    for S, blk in ((1, 0), (5, 0), (64, 0), (2, 32)):
+        say(f"int32 extreme positions hd={hd} S={S} blk={blk}")
+        out, rec = run_gpu(case, S, blk)
+        assert np.array_equal(out[1], np.zeros_like(out[1]))
+        parity(out, _ref(case), f"int32 positions hd={hd} S={S}",
+               "edges nkv 0/1/clamped")
+        check_records(rec, _records(case, S, blk), f"int32 positions S={S}",
+                      "edges nkv 0/1/clamped")
+
+
 def test_7b_2k_split_sweep():
     """28q/4kv hd 128 at nkv 2048 over the swept split counts."""
     case = synth.make_case(2, synth.CFG2, 2048)

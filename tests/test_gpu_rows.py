@@ -104,6 +104,25 @@ def test_rows_full_length(n_q):
 
 
 
+def test_rows_int32_extreme_positions():
+    """Several query rows at positions near the int32 extremes: the rows of
+    positions[b] = INT32_MAX all see the whole cache (clamped), those of
+    INT32_MIN none (each row's position is computed without overflow)."""
+    T, nkvh, n_q = 64, 2, 4
+    for G, hd in ((7, 128), (2, 64), (1, 16)):
+        nh = G * nkvh
+        q, k, v, p = _rows_case(40 + G, 3, n_q, nh, nkvh, hd, T, [T - 1, 0, 5])
+        p[:] = [2**31 - 1, -2**31, 5]
+        scale = float(np.float32(1 / np.sqrt(hd)))
+        want = oracle.decode_attn_rows(q, k, v, p, nkvh, scale)
+        for S in (1, 8, 16):
+            what = f"rows int32 positions G={G} hd={hd} S={S}"
+            say(what)
+            got, _ = _run_rows(q, k, v, p, S, 0, scale)
+            assert np.array_equal(got[1], np.zeros_like(got[1])), what
+            parity(got, want, what, "rows n_q 1..8, 300 rows")
+
+
 @pytest.mark.parametrize("hd", [64, 128, 256])
 def test_rows_nonfinite_v_only_later_rows_see(hd):
     """The newest cache rows are seen by the later query rows of a block
