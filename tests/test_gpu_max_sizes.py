@@ -59,6 +59,8 @@ def test_largest_cache_slice():
     torch = torch_mod()
     nh, nkvh = 8, 1
     assert (MAX_CTX + 64) * nkvh * HD * 2 < (1 << 32)
+    if torch.cuda.get_device_properties(0).total_memory < (12 << 30):
+        pytest.skip("needs 12 GiB of device memory (two 4 GiB caches)")
     say(f"max sizes: K/V caches of {MAX_CTX} rows x {ROW_BYTES} B")
     k = torch.zeros((1, MAX_CTX, nkvh, HD), dtype=torch.float16, device="cuda")
     v = torch.empty_like(k)
